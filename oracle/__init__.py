@@ -1,0 +1,128 @@
+"""CPU oracle for paged GQA decode / verify attention (float64, plain C).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library in ``paged_kv_gqa_02_amd`` and never imports it.
+
+The arithmetic lives in ``oracle.c`` (sources cited in ``oracle.h``); this
+module only builds that file with gcc and marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, E4M3 = 0, 1, 2
+_CODES = {"f32": F32, "bf16": BF16, "fp8": E4M3}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (strict IEEE, no fast-math)."""
+    if force or not os.path.exists(LIB_PATH):
+        src = os.path.join(_HERE, "oracle.c")
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-fno-fast-math", src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        vp = ctypes.c_void_p
+        i = ctypes.c_int
+        lib.oracle_attention.restype = i
+        lib.oracle_attention.argtypes = [vp, vp, vp, i, i, i, i, i, ctypes.c_double, vp]
+        lib.oracle_paged_attention.restype = i
+        lib.oracle_paged_attention.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, i, vp, i,
+                                               vp, i, i, i, ctypes.c_double, vp, i, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().oracle_bf16_value(int(bits))
+
+
+def e4m3_value(byte: int) -> float:
+    return _load().oracle_e4m3_value(int(byte))
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Plain attention for one sequence.
+
+    q [n][Hq][D], k and v [L][Hkv][D] (any float dtype, converted to float64).
+    Returns [n][Hq][D] float64; row i sees keys 0 .. L - n + i.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    n, hq, d = q.shape
+    length, hkv, d2 = k.shape
+    if v.shape != k.shape or d2 != d:
+        raise ValueError("shape mismatch")
+    out = np.empty((n, hq, d), dtype=np.float64)
+    rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), length, n, hq, hkv, d,
+                                  float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_attention rejected its arguments (code {rc})")
+    return out
+
+
+def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
+                    seq_lens, q_per_seq: int, scale: float, seqs=None,
+                    k_scale=None, v_scale=None) -> np.ndarray:
+    """Paged attention read straight from the pool, for the listed sequences.
+
+    k_pool / v_pool: [num_pages][Hkv][page_size][D] as float32 (``f32``),
+    uint16 bf16 bits (``bf16``) or uint8 E4M3 bytes (``fp8``).
+    q: [batch][n][Hq][D] float32 or uint16 bf16 bits.  Returns
+    [len(seqs)][n][Hq][D] float64.
+    """
+    k_pool = np.ascontiguousarray(k_pool)
+    v_pool = np.ascontiguousarray(v_pool)
+    q = np.ascontiguousarray(q)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    num_pages, hkv, page_size, d = k_pool.shape
+    batch, n, hq, dq = q.shape
+    if n != q_per_seq or dq != d or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if bt.ndim != 2 or bt.shape[0] != batch or lens.shape != (batch,):
+        raise ValueError("block_table / seq_lens must have one row per sequence")
+    if seqs is None:
+        seqs = np.arange(batch, dtype=np.int32)
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    ks = vs = None
+    if kv_dtype == "fp8":
+        ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+        vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    out = np.empty((len(seqs), n, hq, d), dtype=np.float64)
+    rc = _load().oracle_paged_attention(
+        _ptr(k_pool), _ptr(v_pool), _CODES[kv_dtype], _ptr(ks), _ptr(vs),
+        num_pages, hkv, page_size, d, _ptr(q), _CODES[q_dtype], _ptr(bt), bt.shape[1],
+        _ptr(lens), batch, n, hq, float(scale), _ptr(seqs), len(seqs), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_attention rejected its arguments (code {rc})")
+    return out

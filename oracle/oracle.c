@@ -1,0 +1,175 @@
+/*
+ * oracle.c -- float64 CPU reference for paged GQA decode / verify attention.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark; never by the product path.  Every step
+ * is the plain definition (full softmax, no tiling, no reordering); the
+ * sources for each function are listed in oracle.h.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* bfloat16 is the upper half of an IEEE binary32: widen and reinterpret. */
+double oracle_bf16_value(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/*
+ * OCP 8-bit floating point, E4M3 variant: 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+ * (mantissa/8 * 2^-6); there are no infinities and S.1111.111 is NaN.
+ */
+double oracle_e4m3_value(uint8_t byte)
+{
+    int sign = (byte >> 7) & 1;
+    int e = (byte >> 3) & 0xF;
+    int m = byte & 0x7;
+    double mag;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+int oracle_attention(const double* q, const double* k, const double* v,
+                     int L, int n, int Hq, int Hkv, int D, double scale,
+                     double* out)
+{
+    if (n < 1 || L < n || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || D < 1)
+        return ORACLE_BAD_ARG;
+    const int G = Hq / Hkv;
+    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!z)
+        return ORACLE_NO_MEMORY;
+
+    for (int i = 0; i < n; ++i) {
+        /* row i is token L - n + i and sees itself and every earlier key */
+        const int visible = L - n + i + 1;
+        for (int h = 0; h < Hq; ++h) {
+            const int hk = h / G;
+            const double* qr = q + ((size_t)i * Hq + h) * D;
+            double zmax = -INFINITY;
+            for (int t = 0; t < visible; ++t) {
+                const double* kt = k + ((size_t)t * Hkv + hk) * D;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += qr[d] * kt[d];
+                z[t] = scale * dot;
+                if (z[t] > zmax)
+                    zmax = z[t];
+            }
+            double denom = 0.0;
+            for (int t = 0; t < visible; ++t) {
+                z[t] = exp(z[t] - zmax);
+                denom += z[t];
+            }
+            double* o = out + ((size_t)i * Hq + h) * D;
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int t = 0; t < visible; ++t)
+                    acc += z[t] * v[((size_t)t * Hkv + hk) * D + d];
+                o[d] = acc / denom;
+            }
+        }
+    }
+    free(z);
+    return ORACLE_OK;
+}
+
+/* value of element `idx` of an array of the given element code */
+static double element(const void* base, int code, size_t idx)
+{
+    switch (code) {
+    case ORACLE_F32:
+        return (double)((const float*)base)[idx];
+    case ORACLE_BF16:
+        return oracle_bf16_value(((const uint16_t*)base)[idx]);
+    case ORACLE_E4M3:
+        return oracle_e4m3_value(((const uint8_t*)base)[idx]);
+    default:
+        return NAN;
+    }
+}
+
+int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
+                           const float* k_scale, const float* v_scale,
+                           int num_pages, int Hkv, int page_size, int D,
+                           const void* q, int q_dtype,
+                           const int32_t* block_table, int max_pages,
+                           const int32_t* seq_lens, int batch, int n, int Hq,
+                           double scale, const int32_t* seqs, int nseqs,
+                           double* out)
+{
+    if (!k_pool || !v_pool || !q || !block_table || !seq_lens || !out || !seqs)
+        return ORACLE_BAD_ARG;
+    if (kv_dtype != ORACLE_F32 && kv_dtype != ORACLE_BF16 && kv_dtype != ORACLE_E4M3)
+        return ORACLE_BAD_ARG;
+    if (q_dtype != ORACLE_F32 && q_dtype != ORACLE_BF16)
+        return ORACLE_BAD_ARG;
+    if (kv_dtype == ORACLE_E4M3 && (!k_scale || !v_scale))
+        return ORACLE_BAD_ARG;
+    if (num_pages < 1 || Hkv < 1 || page_size < 1 || D < 1 || max_pages < 1 ||
+        batch < 1 || n < 1 || Hq < Hkv || Hq % Hkv != 0 || nseqs < 0)
+        return ORACLE_BAD_ARG;
+
+    for (int s = 0; s < nseqs; ++s) {
+        const int b = seqs[s];
+        if (b < 0 || b >= batch)
+            return ORACLE_BAD_ARG;
+        const int L = seq_lens[b];
+        if (L < n || L > page_size * max_pages)
+            return ORACLE_BAD_TABLE;
+
+        double* kc = (double*)malloc(sizeof(double) * (size_t)L * Hkv * D);
+        double* vc = (double*)malloc(sizeof(double) * (size_t)L * Hkv * D);
+        double* qc = (double*)malloc(sizeof(double) * (size_t)n * Hq * D);
+        if (!kc || !vc || !qc) {
+            free(kc); free(vc); free(qc);
+            return ORACLE_NO_MEMORY;
+        }
+
+        /* follow the block table: logical token t -> (page, slot) */
+        int bad = 0;
+        for (int t = 0; t < L && !bad; ++t) {
+            const int page = block_table[(size_t)b * max_pages + t / page_size];
+            const int slot = t % page_size;
+            if (page < 0 || page >= num_pages) {
+                bad = 1;
+                break;
+            }
+            for (int hk = 0; hk < Hkv; ++hk) {
+                double ks = 1.0, vs = 1.0;
+                if (kv_dtype == ORACLE_E4M3) {
+                    ks = (double)k_scale[(size_t)page * Hkv + hk];
+                    vs = (double)v_scale[(size_t)page * Hkv + hk];
+                }
+                const size_t src = (((size_t)page * Hkv + hk) * page_size + slot) * D;
+                const size_t dst = ((size_t)t * Hkv + hk) * D;
+                for (int d = 0; d < D; ++d) {
+                    kc[dst + d] = element(k_pool, kv_dtype, src + d) * ks;
+                    vc[dst + d] = element(v_pool, kv_dtype, src + d) * vs;
+                }
+            }
+        }
+        for (size_t e = 0; e < (size_t)n * Hq * D; ++e)
+            qc[e] = element(q, q_dtype, (size_t)b * n * Hq * D + e);
+
+        int rc = bad ? ORACLE_BAD_TABLE
+                     : oracle_attention(qc, kc, vc, L, n, Hq, Hkv, D, scale,
+                                        out + (size_t)s * n * Hq * D);
+        free(kc); free(vc); free(qc);
+        if (rc != ORACLE_OK)
+            return rc;
+    }
+    return ORACLE_OK;
+}

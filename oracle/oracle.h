@@ -1,0 +1,95 @@
+/*
+ * oracle.h -- CPU reference for paged GQA decode / verify attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct float64
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header, table or constant with the GPU library, and the
+ * product path never calls it.
+ *
+ * Sources (the three web pages this work follows):
+ *  - "Latency and cost in production" (ch. 10), §10.3.1: the current token's
+ *    query is compared with the key of every earlier token to get scores,
+ *    and the values of the high-scoring tokens are gathered.
+ *  - same page, §10.1.2: softmax over the scores; GQA splits the query heads
+ *    into groups, each group sharing one key/value head.
+ *  - same page, §10.4.2 (Fig. 10.4.2) and "Batching, speculative decoding,
+ *    paged attention" §5.3.7: a per-request block table maps logical block i
+ *    to a physical block of 16 tokens anywhere in a shared pool.
+ *  - "Speculative decoding principles" (7.2.1), "the four steps of one
+ *    iteration": the target scores the context plus K draft tokens in one
+ *    forward; each row attends only to itself and earlier positions.
+ *  - "Latency and cost in production" §10.8.2-§10.8.3: real ~= (q - zp) *
+ *    scale, symmetric quantisation has zp = 0.
+ *
+ * Readings where the pages are silent (restated in the design doc):
+ *  - softmax uses the natural exponential of scale * q.k;
+ *  - seq_lens[b] counts every key already in the pool, including the n new
+ *    query tokens; row i (0 <= i < n) sees keys 0 .. L - n + i inclusive;
+ *  - query head h uses key/value head floor(h / (Hq / Hkv));
+ *  - fp8 is OCP E4M3 (bias 7, max 448, S.1111.111 is NaN), dequantised as
+ *    value(byte) * scale[page][kv_head] with zero-point 0.
+ */
+#ifndef PAGED_ATTN_ORACLE_H
+#define PAGED_ATTN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element codes of the oracle's own decoder */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_E4M3 = 2 };
+
+/* return codes */
+enum { ORACLE_OK = 0, ORACLE_BAD_ARG = -1, ORACLE_BAD_TABLE = -2, ORACLE_NO_MEMORY = -3 };
+
+/* Exact value of a bfloat16 bit pattern (the top 16 bits of an IEEE binary32). */
+double oracle_bf16_value(uint16_t bits);
+
+/* Exact value of an OCP E4M3 byte; NaN for 0x7F and 0xFF. */
+double oracle_e4m3_value(uint8_t byte);
+
+/*
+ * Plain attention for ONE sequence over contiguous keys and values.
+ *   q   [n][Hq][D]     query rows (row i is the (L - n + i)-th token)
+ *   k,v [L][Hkv][D]    every key / value of the sequence in logical order
+ *   out [n][Hq][D]
+ * Row i, head h: z_t = scale * sum_d q[i][h][d] * k[t][h/G][d] for
+ * t = 0 .. L - n + i; out = sum_t exp(z_t - max z) v_t / sum_t exp(z_t - max z).
+ * Returns ORACLE_BAD_ARG unless 1 <= n <= L, Hkv >= 1, Hq % Hkv == 0, D >= 1.
+ */
+int oracle_attention(const double* q, const double* k, const double* v,
+                     int L, int n, int Hq, int Hkv, int D, double scale,
+                     double* out);
+
+/*
+ * Paged attention for the listed sequences, read straight from the pool.
+ *   k_pool, v_pool  [num_pages][Hkv][page_size][D] elements of kv_dtype
+ *                   (float32, bfloat16 bits, or E4M3 bytes)
+ *   k_scale,v_scale [num_pages][Hkv] float32, used only for E4M3
+ *   q               [batch][n][Hq][D] elements of q_dtype (float32 or bf16)
+ *   block_table     [batch][max_pages] int32
+ *   seq_lens        [batch] int32
+ *   seqs            [nseqs] sequence indices to evaluate
+ *   out             [nseqs][n][Hq][D] float64
+ * Token t of sequence b is slot t % page_size of physical page
+ * block_table[b][t / page_size].  Returns ORACLE_BAD_TABLE when a page id
+ * the sequence needs lies outside [0, num_pages) or L is outside [n,
+ * page_size * max_pages].
+ */
+int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
+                           const float* k_scale, const float* v_scale,
+                           int num_pages, int Hkv, int page_size, int D,
+                           const void* q, int q_dtype,
+                           const int32_t* block_table, int max_pages,
+                           const int32_t* seq_lens, int batch, int n, int Hq,
+                           double scale, const int32_t* seqs, int nseqs,
+                           double* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

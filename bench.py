@@ -1,0 +1,177 @@
+"""Benchmark of the paged GQA decode / verify attention hot path on one MI355X.
+
+Default: the 8B-GQA decode layer (batch 64, one query row, 32 query heads / 8
+KV heads, head_dim 128, context 2048, page size 16, bf16 K/V/Q, block tables
+from a seeded shuffled free list).  One step = one paged_attn_verify call
+(partition kernel, plus the split-K reduce when the plan splits) over the
+whole batch; inputs are resident in HBM and a 1 GiB buffer is overwritten
+before every step so that no K/V byte is served from L2 or the MALL.
+
+Prints ONE JSON line (rank 0).  `value` is effective HBM GB/s: (K + V bytes of
+every token of every sequence, fp8 scales, Q, O) / mean call time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+import workloads as W
+
+METRIC = "decode attention effective HBM GB/s (% of peak) + tokens/s, B=64 ctx=2048"
+PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 1 << 30
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode8b", choices=W.WORKLOADS)
+    ap.add_argument("--partition-pages", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def cpu_baseline(case, reps):
+    """The float64 oracle, as it is, over the whole batch on every host core."""
+    import concurrent.futures as cf
+    import oracle
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(cores, 16))
+
+    def one(b):
+        oracle.paged_attention(case.k_pool, case.v_pool, case.kv_dtype, case.q, case.q_dtype,
+                               case.block_table, case.seq_lens, case.q_per_seq, case.scale,
+                               seqs=[b], k_scale=case.k_scale, v_scale=case.v_scale)
+
+    times = []
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        for r in range(reps):
+            t0 = time.perf_counter()
+            list(ex.map(one, range(case.batch)))
+            times.append(time.perf_counter() - t0)
+            log(f"cpu baseline rep {r}: {times[-1]:.2f} s")
+    t = float(np.median(times))
+    return {"value": case.algorithmic_bytes() / t / 1e9, "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"whole batch ({case.batch} sequences, every head and row) x {reps} reps, "
+                      f"median {t:.3f} s, float64 C oracle, one sequence per thread",
+            "tokens_per_s": case.batch * case.q_per_seq / t}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_gqa_02_amd as pa
+    from workloads.device import to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    log(f"generating {args.workload}")
+    case = W.workload(args.workload)
+    dev = to_device(case)
+    pool = pa.paged_attn_create_pool(dev.k, dev.v, dev.k_scale, dev.v_scale,
+                                     args.partition_pages)
+    plan = pa.paged_attn_plan(pool, case.batch, case.q_per_seq, case.num_q_heads,
+                              case.max_seq_len)
+    out = torch.empty_like(dev.q)
+    ws = pa.workspace_for(pool, dev.q, case.max_seq_len)
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if flush is not None:
+            flush.fill_(1)
+        if evs is None:
+            pa.paged_attn_verify(pool, dev.q, out, dev.block_table, dev.seq_lens,
+                                 case.max_seq_len, case.scale, ws)
+        else:
+            c0, k0, k1, c1 = evs
+            c0.record(stream)
+            pa.paged_attn_verify(pool, dev.q, out, dev.block_table, dev.seq_lens,
+                                 case.max_seq_len, case.scale, ws, ev_begin=k0, ev_end=k1)
+            c1.record(stream)
+
+    log(f"plan {plan}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[pa.HipEvent() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([e[0].elapsed_ms(e[3]) for e in evs])
+    kern_ms = np.array([e[1].elapsed_ms(e[2]) for e in evs])
+    log(f"timed {args.steps} steps: call {call_ms.mean() * 1e3:.1f} us, "
+        f"partition kernel {kern_ms.mean() * 1e3:.1f} us")
+
+    nbytes = case.algorithmic_bytes()
+    call_s = float(call_ms.mean()) / 1e3
+    kern_s = float(kern_ms.mean()) / 1e3
+    gbs = nbytes / call_s / 1e9
+    achieved = nbytes / kern_s / 1e9
+    rows = case.batch * case.q_per_seq
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(call_ms.mean()), 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q", "f32": "f32"}[case.kv_dtype],
+        "data": "synthetic (seeded N(0,1), shuffled page pool)",
+        "config": {"workload": case.name, "batch": case.batch, "q_per_seq": case.q_per_seq,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "seq_len_max": case.max_seq_len,
+                   "seq_len_mean": float(case.seq_lens.mean()), "page_size": W.PAGE_SIZE,
+                   "kv_dtype": case.kv_dtype, "bytes_per_call": nbytes},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(rows / call_s, 1),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "call_us": {"mean": round(float(call_ms.mean()) * 1e3, 2),
+                    "p10": round(float(np.percentile(call_ms, 10)) * 1e3, 2),
+                    "p50": round(float(np.percentile(call_ms, 50)) * 1e3, 2),
+                    "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
+        "plan": plan,
+        "roofline": {"bound": "hbm", "kernel": "paged_attn_partition",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel_us_mean": round(kern_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

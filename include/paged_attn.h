@@ -1,0 +1,176 @@
+/*
+ * paged_attn.h -- C ABI of libpaged_attn: paged GQA decode and speculative
+ * verify attention for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (sources: "Latency and cost in production" ch. 10,
+ * §10.3.1, §10.1.2, §10.4.2; "Batching, speculative decoding, paged
+ * attention" §5.3.7; "Speculative decoding principles" 7.2.1, "the four
+ * steps of one iteration"):
+ *
+ *   For sequence b with L = seq_lens[b] tokens already in the pool and n
+ *   query rows (n = 1 for decode, K + 1 for verify), row i (0 <= i < n) is
+ *   token L - n + i and attends to keys t = 0 .. L - n + i (itself and every
+ *   earlier token; later draft rows are masked).  Query head h reads
+ *   key/value head floor(h / G), G = num_q_heads / num_kv_heads.  Token t
+ *   lives in slot t % 16 of physical page block_table[b][t / 16].
+ *
+ *     out[b][i][h] = sum_t softmax_t(scale * q[b][i][h] . K_t) * V_t
+ *
+ *   fp8 pools store OCP E4M3 bytes; the value of a key/value element is
+ *   value(byte) * scale[page][kv_head] (symmetric, zero-point 0:
+ *   "Latency and cost in production" §10.8.2-§10.8.3).
+ *
+ * Layouts (all row-major, all device memory unless noted):
+ *   K pool, V pool   [num_pages][num_kv_heads][16][128] elements of kv_dtype
+ *   k_scale, v_scale [num_pages][num_kv_heads] float32 (fp8 pools only)
+ *   q, out           [batch][q_per_seq][num_q_heads][128] elements of q_dtype
+ *                    (out has the dtype of q)
+ *   block_table      [batch][max_pages_per_seq] int32
+ *   seq_lens         [batch] int32
+ *   workspace        paged_attn_workspace_bytes() bytes, 256-byte aligned
+ *
+ * Supported element types: (kv f32, q f32), (kv bf16, q bf16),
+ * (kv fp8-e4m3, q bf16).  page_size must be 16 and head_dim 128.
+ *
+ * Ownership: every buffer belongs to the caller.  The library allocates no
+ * device memory; a pool handle only records the descriptor (a few dozen
+ * bytes of host memory) and never frees the caller's arrays.
+ *
+ * Calls: asynchronous on the given stream (a hipStream_t; NULL = the null
+ * stream of the current device) on the current HIP device.  Argument checks
+ * run on the host before anything is launched and return an error without
+ * launching.  Calls are reentrant; a pool handle is read-only after
+ * creation and may be shared across threads.
+ *
+ * Device-array contract (not checked on the fast path; paged_attn_validate
+ * checks it): for every b, n <= seq_lens[b] <= max_seq_len <=
+ * 16 * max_pages_per_seq, and block_table[b][p] lies in [0, num_pages) for
+ * p < ceil(seq_lens[b] / 16).  Entries past a sequence's last page, slots
+ * past its last token and pages no table names are never read and may hold
+ * anything (NaN included).  Two tables may name the same page.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,  /* null pointer, bad size or count */
+    PA_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels handle */
+    PA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+    PA_ERR_HIP = -4,          /* a HIP runtime call failed; see paged_attn_last_error() */
+    PA_ERR_CONTRACT = -5      /* paged_attn_validate found a bad device array */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F32 = 0,
+    PA_BF16 = 1,
+    PA_FP8_E4M3 = 2
+} pa_dtype;
+
+/* Description of a page pool.  All pointers are device pointers. */
+typedef struct pa_pool_desc {
+    int32_t num_pages;
+    int32_t page_size;        /* must be 16 */
+    int32_t num_kv_heads;
+    int32_t head_dim;         /* must be 128 */
+    pa_dtype kv_dtype;
+    const void* k;            /* [num_pages][num_kv_heads][16][128] */
+    const void* v;            /* same layout as k */
+    const float* k_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
+    const float* v_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
+    int32_t partition_pages;  /* split-K partition length in pages; 0 = chosen per call */
+} pa_pool_desc;
+
+typedef struct pa_pool pa_pool;
+
+/* How one call is split across the GPU (for reporting and tests). */
+typedef struct pa_plan {
+    int32_t partition_pages;  /* pages per context partition */
+    int32_t num_splits;       /* partitions of the longest sequence */
+    int32_t row_tiles;        /* 16-row MFMA tiles per workgroup */
+    int32_t row_chunks;       /* workgroups needed to cover the G * n rows */
+    int32_t waves;            /* waves per workgroup */
+    int32_t grid;             /* workgroups of the partition kernel */
+    int32_t reduce;           /* 1 if the split-K reduce kernel runs */
+} pa_plan;
+
+/* Bytes of the K and V pool arrays for a pool of this shape (host only). */
+pa_status paged_attn_pool_bytes(int32_t num_pages, int32_t page_size,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                pa_dtype kv_dtype, size_t* k_bytes, size_t* v_bytes);
+
+/* Checks the descriptor and returns a handle recording it (host only, no HIP call).
+ * PA_ERR_INVALID_ARG for null pointers or counts < 1, PA_ERR_UNSUPPORTED for
+ * page_size != 16, head_dim != 128 or an unknown dtype; *out is NULL on error. */
+pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out);
+
+/* Frees the handle only; the pool arrays stay with the caller.  NULL is a no-op. */
+void paged_attn_destroy_pool(pa_pool* pool);
+
+/* The split the library will use for a call of this shape (host only). */
+pa_status paged_attn_plan(const pa_pool* pool, int32_t batch, int32_t q_per_seq,
+                          int32_t num_q_heads, int32_t max_seq_len, pa_plan* plan);
+
+/* Workspace bytes a call of this shape needs (0 when it runs unsplit). */
+pa_status paged_attn_workspace_bytes(const pa_pool* pool, int32_t batch,
+                                     int32_t q_per_seq, int32_t num_q_heads,
+                                     int32_t max_seq_len, size_t* bytes);
+
+/* Decode: one query row per sequence (q_per_seq = 1).  The newest token's K/V
+ * must already be in the pool (seq_lens counts it).  max_seq_len is a host-side
+ * upper bound of seq_lens used to size the split. */
+pa_status paged_attn_decode(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                            void* out, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* seq_lens,
+                            int32_t max_seq_len, int32_t batch, int32_t num_q_heads,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Verify: q_per_seq = K + 1 query rows per sequence (the last accepted token
+ * and the K drafts, whose K/V are already appended), scored in one call under
+ * the causal mask described at the top of this file. */
+pa_status paged_attn_verify(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                            void* out, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* seq_lens,
+                            int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                            int32_t num_q_heads, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* paged_attn_verify that also records ev_begin right before the attention
+ * (partition) kernel and ev_end right after it on the same stream, so a
+ * caller can time that kernel alone.  The events are hipEvent_t handles
+ * created by the caller; either may be NULL. */
+pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                                  void* out, const int32_t* block_table,
+                                  int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                  int32_t num_q_heads, float scale, void* workspace,
+                                  size_t workspace_bytes, void* stream,
+                                  void* ev_begin, void* ev_end);
+
+/* Debug check of the device-array contract: copies block_table and seq_lens
+ * to the host (synchronously, on `stream`) and returns PA_ERR_CONTRACT if a
+ * length or a needed page id is out of range. */
+pa_status paged_attn_validate(const pa_pool* pool, const int32_t* block_table,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens,
+                              int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                              void* stream);
+
+/* Static description of a status code. */
+const char* paged_attn_status_str(pa_status status);
+
+/* Text of the last error recorded on the calling thread ("" if none). */
+const char* paged_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,937 @@
+// paged_attn.hip -- paged GQA decode / verify attention for MI355X (gfx950).
+//
+// The operation is defined in include/paged_attn.h.  Sources: "Latency and
+// cost in production" ch. 10 (§10.3.1 attention over every earlier key,
+// §10.1.2 softmax / online softmax / GQA groups, §10.4.2 block table,
+// §10.8.2-§10.8.3 symmetric scale); "Batching, speculative decoding, paged
+// attention" §5.3.1 (decode is HBM-bound) and §5.3.7 (the kernel follows the
+// block table to gather scattered 16-token blocks); "Speculative decoding
+// principles" 7.2.1 (one forward scores K + 1 positions under a causal mask).
+//
+// Design (gfx950, wave64):
+//  * One workgroup = one (sequence, kv head, row chunk, context partition).
+//    Its waves walk the partition's pages round-robin; every K/V byte is read
+//    from HBM once per (sequence, kv head) and used by all G * n query rows
+//    of the group at once.
+//  * QK^T and PV run on MFMA with the tokens of one page as the 16-wide M /
+//    K dimension and the group's query rows as N (padded to 16 per tile), so
+//    the GQA group and the verify rows share each K/V fragment in registers.
+//    Pages are loaded straight from HBM into VGPRs in the MFMA operand
+//    layout: a K fragment is 16 rows x 64 contiguous bytes per instruction, a
+//    V fragment 4 full 256-byte rows; V is transposed in registers with
+//    v_perm.  The QK output layout is exactly the PV B-operand layout, so the
+//    probabilities never leave their lanes.
+//  * Online softmax in the log2 domain (scale * log2 e folded into the
+//    scores, v_exp_f32), running max reduced across the 4 lane groups with
+//    two shuffles per page; the running sum stays lane-local until the end.
+//  * Waves of a workgroup are merged in LDS in a fixed order; context
+//    partitions (split-K) are merged by a second small kernel.  Both merges
+//    use the same rescaling: weight 2^(m_part - m_max).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "paged_attn.h"
+
+#define PA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kHeadDim = 128;
+constexpr int kSlab = kPage * kHeadDim;     // elements of one (page, kv head) slab
+constexpr int kWave = 64;
+constexpr int kMaxRowTiles = 4;             // 16-row MFMA tiles per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+// Running max before any key is seen.  Finite, so exp2(m_old - m_new) is
+// never inf - inf; masked scores are -inf and give exp2(-inf) = 0.
+constexpr float kNoMax = -1.0e30f;
+constexpr int kAccStride = kHeadDim + 4;    // LDS row stride of the wave merge (bank skew)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+struct Args {
+    const void* k;
+    const void* v;
+    const float* k_scale;
+    const float* v_scale;
+    const void* q;
+    void* out;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    float* part_acc;       // [B][n][Hq][num_splits][128]
+    float* part_ml;        // [B][n][Hq][num_splits][2]  (max in log2 units, sum)
+    int64_t page_stride;   // elements from one page to the next (Hkv * 16 * 128)
+    int32_t num_pages;
+    int32_t max_pages;
+    int32_t n;
+    int32_t hq;
+    int32_t hkv;
+    int32_t group;         // G = Hq / Hkv
+    int32_t rows;          // G * n query rows per (sequence, kv head)
+    int32_t row_chunks;
+    int32_t num_splits;
+    int32_t part_pages;
+    float scale_log2;      // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_bits(float x)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ float bf16_float(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+// Two E4M3 bytes (low or high half of w) -> two bf16 in one dword.  E4M3 is
+// a subset of bf16, so the conversion is exact.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
+{
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 E4M3 bytes -> 8 bf16
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
+{
+    u32x4 r;
+    r[0] = fp8x2_to_bf16x2<false>(w0);
+    r[1] = fp8x2_to_bf16x2<true>(w0);
+    r[2] = fp8x2_to_bf16x2<false>(w1);
+    r[3] = fp8x2_to_bf16x2<true>(w1);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// one page of K and V for one kv head, in MFMA operand layout
+//   l16 = lane % 16, g = lane / 16
+//   K: lane holds token l16; V: lane holds tokens 4g..4g+3, dims 8*l16..+7
+// ---------------------------------------------------------------------------
+template <int KV> struct Page;
+
+template <> struct Page<KV_BF16> {
+    u32x4 k[4];   // k[c]: K[l16][32c + 8g .. +8]
+    u32x4 v[4];   // v[s]: V[4g + s][8 l16 .. +8]
+};
+
+template <> struct Page<KV_FP8> {
+    u32x4 k[2];   // k[h]: K[l16][64h + 16g .. +16] bytes
+    u32x2 v[4];   // v[s]: V[4g + s][8 l16 .. +8] bytes
+    float ks, vs;
+};
+
+template <> struct Page<KV_F32> {
+    f32x4 k[8];   // k[c]: K[l16][16c + 4g .. +4]
+    f32x4 v[8];   // v[2s + h]: V[4g + s][8 l16 + 4h .. +4]
+};
+
+__device__ __forceinline__ void load_page(Page<KV_BF16>& p, const Args& a, int phys, int kh,
+                                          int l16, int g)
+{
+    const int64_t off = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
+    const uint16_t* kb = static_cast<const uint16_t*>(a.k) + off;
+    const uint16_t* vb = static_cast<const uint16_t*>(a.v) + off;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kb + l16 * kHeadDim + 8 * g);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vb + 4 * g * kHeadDim + 8 * l16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) p.k[c] = kp[4 * c];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) p.v[s] = vp[16 * s];
+}
+
+__device__ __forceinline__ void load_page(Page<KV_FP8>& p, const Args& a, int phys, int kh,
+                                          int l16, int g)
+{
+    const int64_t off = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
+    const uint8_t* kb = static_cast<const uint8_t*>(a.k) + off;
+    const uint8_t* vb = static_cast<const uint8_t*>(a.v) + off;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kb + l16 * kHeadDim + 16 * g);
+    const u32x2* vp = reinterpret_cast<const u32x2*>(vb + 4 * g * kHeadDim + 8 * l16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) p.k[h] = kp[4 * h];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) p.v[s] = vp[16 * s];
+    const int64_t si = (int64_t)phys * a.hkv + kh;
+    p.ks = a.k_scale[si];
+    p.vs = a.v_scale[si];
+}
+
+__device__ __forceinline__ void load_page(Page<KV_F32>& p, const Args& a, int phys, int kh,
+                                          int l16, int g)
+{
+    const int64_t off = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
+    const float* kb = static_cast<const float*>(a.k) + off;
+    const float* vb = static_cast<const float*>(a.v) + off;
+    const f32x4* kp = reinterpret_cast<const f32x4*>(kb + l16 * kHeadDim + 4 * g);
+    const f32x4* vp = reinterpret_cast<const f32x4*>(vb + 4 * g * kHeadDim + 8 * l16);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) p.k[c] = kp[4 * c];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        p.v[2 * s] = vp[32 * s];
+        p.v[2 * s + 1] = vp[32 * s + 1];
+    }
+}
+
+// zero the V rows of tokens at or past the sequence end (their slots may hold NaN)
+__device__ __forceinline__ void clear_dead_v(Page<KV_BF16>& p, int first_dead_s)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        if (s >= first_dead_s) p.v[s] = u32x4{0u, 0u, 0u, 0u};
+}
+__device__ __forceinline__ void clear_dead_v(Page<KV_FP8>& p, int first_dead_s)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        if (s >= first_dead_s) p.v[s] = u32x2{0u, 0u};
+}
+__device__ __forceinline__ void clear_dead_v(Page<KV_F32>& p, int first_dead_s)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        if (s >= first_dead_s) {
+            p.v[2 * s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            p.v[2 * s + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+}
+
+// ---------------------------------------------------------------------------
+// query rows in MFMA B-operand layout (lane holds row l16 of its tile)
+// ---------------------------------------------------------------------------
+template <int KV> struct QFrag;
+template <> struct QFrag<KV_BF16> { bf16x8 b[4]; };   // dims 32c + 8g .. +8
+template <> struct QFrag<KV_FP8>  { bf16x8 b[4]; };   // dims 64(c/2) + 16g + 8(c%2) .. +8
+template <> struct QFrag<KV_F32>  { f32x4 b[8]; };    // dims 16c + 4g .. +4
+
+__device__ __forceinline__ void load_q(QFrag<KV_BF16>& f, const uint16_t* row, bool valid, int g)
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u32x4 x = valid ? *reinterpret_cast<const u32x4*>(row + 32 * c + 8 * g)
+                        : u32x4{0u, 0u, 0u, 0u};
+        f.b[c] = __builtin_bit_cast(bf16x8, x);
+    }
+}
+__device__ __forceinline__ void load_q(QFrag<KV_FP8>& f, const uint16_t* row, bool valid, int g)
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int d0 = 64 * (c >> 1) + 16 * g + 8 * (c & 1);
+        u32x4 x = valid ? *reinterpret_cast<const u32x4*>(row + d0) : u32x4{0u, 0u, 0u, 0u};
+        f.b[c] = __builtin_bit_cast(bf16x8, x);
+    }
+}
+__device__ __forceinline__ void load_q(QFrag<KV_F32>& f, const float* row, bool valid, int g)
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        f.b[c] = valid ? *reinterpret_cast<const f32x4*>(row + 16 * c + 4 * g)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// S^T[token][row] for one 16-row tile: lane holds tokens 4g + v of row l16
+__device__ __forceinline__ f32x4 scores(const Page<KV_BF16>& p, const QFrag<KV_BF16>& q)
+{
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, p.k[c]), q.b[c],
+                                                    s, 0, 0, 0);
+    return s;
+}
+__device__ __forceinline__ f32x4 scores(const Page<KV_FP8>& p, const QFrag<KV_FP8>& q)
+{
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const u32x4& w = p.k[c >> 1];
+        const int h = c & 1;
+        u32x4 kb = fp8x8_to_bf16x8(w[2 * h], w[2 * h + 1]);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), q.b[c], s,
+                                                    0, 0, 0);
+    }
+    return s * p.ks;
+}
+__device__ __forceinline__ f32x4 scores(const Page<KV_F32>& p, const QFrag<KV_F32>& q)
+{
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(p.k[c][e], q.b[c][e], s, 0, 0, 0);
+    return s;
+}
+
+// o[db] holds O[row l16][32g + 8v + db], v = 0..3 (the PV output layout)
+template <int KV> struct Acc { f32x4 o[8]; };
+
+// acc += P * V for one tile; p[s] is the weight of token 4g + s for row l16.
+// Returns the weights as rounded for the product (bf16 paths) so that the
+// running sum uses the same values.
+__device__ __forceinline__ float pv(Acc<KV_BF16>& acc, const Page<KV_BF16>& pg, const float (&p)[4])
+{
+    uint32_t b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = bf16_bits(p[s]);
+    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        const int w = db >> 1;
+        const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(pg.v[1][w], pg.v[0][w], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(pg.v[3][w], pg.v[2][w], sel);
+        const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
+        acc.o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc.o[db], 0, 0, 0);
+    }
+    return bf16_float(b[0]) + bf16_float(b[1]) + bf16_float(b[2]) + bf16_float(b[3]);
+}
+
+__device__ __forceinline__ float pv(Acc<KV_FP8>& acc, const Page<KV_FP8>& pg, const float (&p)[4])
+{
+    uint32_t b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = bf16_bits(p[s] * pg.vs);
+    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
+    u32x4 vb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) vb[s] = fp8x8_to_bf16x8(pg.v[s][0], pg.v[s][1]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        const int w = db >> 1;
+        const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(vb[1][w], vb[0][w], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(vb[3][w], vb[2][w], sel);
+        const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
+        acc.o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc.o[db], 0, 0, 0);
+    }
+    return p[0] + p[1] + p[2] + p[3];
+}
+
+__device__ __forceinline__ float pv(Acc<KV_F32>& acc, const Page<KV_F32>& pg, const float (&p)[4])
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            acc.o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(pg.v[2 * s + (db >> 2)][db & 3], p[s],
+                                                              acc.o[db], 0, 0, 0);
+    return p[0] + p[1] + p[2] + p[3];
+}
+
+template <int KV> struct QPtr { typedef uint16_t type; };
+template <> struct QPtr<KV_F32> { typedef float type; };
+
+template <int KV> struct OutT { typedef uint16_t type; };
+template <> struct OutT<KV_F32> { typedef float type; };
+
+__device__ __forceinline__ void store_out(uint16_t* o, float x) { *o = (uint16_t)bf16_bits(x); }
+__device__ __forceinline__ void store_out(float* o, float x) { *o = x; }
+
+// ---------------------------------------------------------------------------
+// partition kernel
+// ---------------------------------------------------------------------------
+template <int KV, int NT, int W, int PF>
+__global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
+{
+    constexpr int RT = 16 * NT;   // rows per workgroup
+    __shared__ float sm_ml[W][RT][2];
+    __shared__ float sm_acc[RT * kAccStride];
+    __shared__ float sm_fin[RT][2];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
+
+    int unit = blockIdx.x;
+    const int split = unit % a.num_splits;
+    unit /= a.num_splits;
+    const int rc = unit % a.row_chunks;
+    unit /= a.row_chunks;
+    const int kh = unit % a.hkv;
+    const int b = unit / a.hkv;
+
+    // lengths are clamped to what the block table can describe, and page ids
+    // to the pool, so that arrays breaking the contract give wrong numbers
+    // but never an access outside the caller's buffers
+    const int L = min(a.seq_lens[b], a.max_pages * kPage);
+    const int npages = (L + kPage - 1) / kPage;
+    const int nsplit_b = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
+    if (split >= nsplit_b) return;
+    const int pg0 = split * a.part_pages;
+    const int pg1 = min(pg0 + a.part_pages, npages);
+    const int row0 = rc * RT;
+    const int rows_here = min(RT, a.rows - row0);
+    const int first_limit = L - a.n;          // row 0 sees tokens 0 .. L - n
+
+    // query fragments and per-row visibility limits
+    QFrag<KV> qf[NT];
+    int lim[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = row0 + nt * 16 + l16;
+        const bool valid = r < a.rows;
+        const int i = valid ? r / a.group : 0;
+        const int h = kh * a.group + (valid ? r - i * a.group : 0);
+        const typename QPtr<KV>::type* qrow =
+            static_cast<const typename QPtr<KV>::type*>(a.q) +
+            (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim;
+        load_q(qf[nt], qrow, valid, g);
+        lim[nt] = valid ? first_limit + i : L - 1;
+    }
+
+    Acc<KV> acc[NT];
+    float m[NT], l[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[nt].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[nt] = kNoMax;
+        l[nt] = 0.f;
+    }
+
+    // this wave's pages: pg0 + wave + j * W, j < nj (nj <= 64 by construction)
+    const int nj = (pg1 - pg0 - wave + W - 1) / W;
+    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+    const int my_id = (lane < nj) ? min(max(bt_row[pg0 + wave + lane * W], 0), a.num_pages - 1)
+                                  : 0;
+
+    auto consume = [&](Page<KV>& pg, int j) {
+        const int base = (pg0 + wave + j * W) * kPage;
+        if (base + kPage > L) clear_dead_v(pg, (L - base - 4 * g));
+        const bool need_mask = base + kPage - 1 > first_limit;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 sv = scores(pg, qf[nt]);
+            float s[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s[v] = sv[v] * a.scale_log2;
+            if (need_mask) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    s[v] = (base + 4 * g + v <= lim[nt]) ? s[v] : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(m[nt], mx);
+            const float alpha = fast_exp2(m[nt] - mnew);
+            m[nt] = mnew;
+            float p[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mnew);
+#pragma unroll
+            for (int db = 0; db < 8; ++db) acc[nt].o[db] *= alpha;
+            l[nt] = l[nt] * alpha + pv(acc[nt], pg, p);
+        }
+    };
+
+    Page<KV> buf[PF];
+#pragma unroll
+    for (int st = 0; st < PF - 1; ++st)
+        if (st < nj) load_page(buf[st], a, __builtin_amdgcn_readlane(my_id, st), kh, l16, g);
+
+    for (int j0 = 0; j0 < nj; j0 += PF) {
+#pragma unroll
+        for (int st = 0; st < PF; ++st) {
+            const int j = j0 + st;
+            if (j < nj) {
+                const int jn = j + PF - 1;
+                if (jn < nj)
+                    load_page(buf[(st + PF - 1) % PF], a, __builtin_amdgcn_readlane(my_id, jn),
+                              kh, l16, g);
+                consume(buf[st], j);
+            }
+        }
+    }
+
+    // ---- merge the waves of this workgroup (fixed order) ----
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        l[nt] += __shfl_xor(l[nt], 16);
+        l[nt] += __shfl_xor(l[nt], 32);
+        if (g == 0) {
+            sm_ml[wave][nt * 16 + l16][0] = m[nt];
+            sm_ml[wave][nt * 16 + l16][1] = l[nt];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int row = nt * 16 + l16;
+        float mm = kNoMax;
+#pragma unroll
+        for (int w = 0; w < W; ++w) mm = fmaxf(mm, sm_ml[w][row][0]);
+        const float fac = fast_exp2(m[nt] - mm);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[nt].o[db] *= fac;
+        if (wave == 0 && g == 0) {
+            float ls = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) ls += sm_ml[w][row][1] * fast_exp2(sm_ml[w][row][0] - mm);
+            sm_fin[row][0] = mm;
+            sm_fin[row][1] = ls;
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int row = nt * 16 + l16;
+                if (row < rows_here) {
+                    float* dst = sm_acc + row * kAccStride + 32 * g;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) {
+                            if (w == 0) dst[8 * v + db] = acc[nt].o[db][v];
+                            else dst[8 * v + db] += acc[nt].o[db][v];
+                        }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: final output (one partition) or a split-K partial ----
+    const bool single = nsplit_b == 1;
+    for (int e = threadIdx.x; e < rows_here * kHeadDim; e += W * kWave) {
+        const int row = e / kHeadDim;
+        const int d = e - row * kHeadDim;
+        const int r = row0 + row;
+        const int i = r / a.group;
+        const int h = kh * a.group + (r - i * a.group);
+        const int64_t orow = ((int64_t)b * a.n + i) * a.hq + h;
+        const float x = sm_acc[row * kAccStride + d];
+        if (single) {
+            typename OutT<KV>::type* o = static_cast<typename OutT<KV>::type*>(a.out);
+            store_out(o + orow * kHeadDim + d, x / sm_fin[row][1]);
+        } else {
+            const int64_t pidx = orow * a.num_splits + split;
+            a.part_acc[pidx * kHeadDim + d] = x;
+            if (d == 0) {
+                a.part_ml[pidx * 2] = sm_fin[row][0];
+                a.part_ml[pidx * 2 + 1] = sm_fin[row][1];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// split-K reduce: one wave per (sequence, query row, head), two dims per lane
+// ---------------------------------------------------------------------------
+template <typename OT>
+__global__ __launch_bounds__(kWave) void paged_attn_reduce(Args a)
+{
+    const int64_t orow = blockIdx.x;                 // (b * n + i) * hq + h
+    const int b = (int)(orow / ((int64_t)a.n * a.hq));
+    const int L = min(a.seq_lens[b], a.max_pages * kPage);
+    const int npages = (L + kPage - 1) / kPage;
+    const int ns = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
+    if (ns <= 1) return;                             // written by the partition kernel
+    const float* ml = a.part_ml + orow * a.num_splits * 2;
+    float mm = kNoMax;
+    for (int s = 0; s < ns; ++s) mm = fmaxf(mm, ml[2 * s]);
+    const int d = 2 * threadIdx.x;
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    const float* pa = a.part_acc + orow * a.num_splits * kHeadDim + d;
+    for (int s = 0; s < ns; ++s) {
+        const float w = fast_exp2(ml[2 * s] - mm);
+        lsum += ml[2 * s + 1] * w;
+        o0 += pa[s * kHeadDim] * w;
+        o1 += pa[s * kHeadDim + 1] * w;
+    }
+    OT* out = static_cast<OT*>(a.out) + orow * kHeadDim + d;
+    store_out(out, o0 / lsum);
+    store_out(out + 1, o1 / lsum);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* what)
+{
+    g_last_error = what;
+    return st;
+}
+
+pa_status hip_fail(hipError_t e, const char* where)
+{
+    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    return PA_ERR_HIP;
+}
+
+int cu_count()
+{
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+constexpr int kWaves = 8;        // waves per workgroup of the partition kernel
+constexpr int kPrefetch = 2;     // pages held in registers per wave (1 in flight + 1 in use)
+
+size_t elem_size(pa_dtype t)
+{
+    return t == PA_F32 ? 4 : t == PA_BF16 ? 2 : 1;
+}
+
+bool dtype_known(pa_dtype t) { return t == PA_F32 || t == PA_BF16 || t == PA_FP8_E4M3; }
+
+}  // namespace
+
+struct pa_pool {
+    pa_pool_desc d;
+};
+
+namespace {
+
+pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, int32_t max_len,
+                    pa_plan* pl)
+{
+    if (!pool || !pl) return fail(PA_ERR_INVALID_ARG, "null pool or plan");
+    const pa_pool_desc& d = pool->d;
+    if (batch < 1 || n < 1 || hq < 1 || max_len < 1)
+        return fail(PA_ERR_INVALID_ARG, "batch, q_per_seq, num_q_heads and max_seq_len must be >= 1");
+    if (hq < d.num_kv_heads || hq % d.num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+    if (max_len < n) return fail(PA_ERR_INVALID_ARG, "max_seq_len < q_per_seq");
+    const int64_t rows = (int64_t)(hq / d.num_kv_heads) * n;
+    if (rows > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many query rows");
+    const int nt = (int)std::min<int64_t>(kMaxRowTiles, (rows + 15) / 16);
+    const int64_t row_chunks = (rows + 16 * nt - 1) / (16 * nt);
+    const int max_pages = (max_len + kPage - 1) / kPage;
+    const int64_t units = (int64_t)batch * d.num_kv_heads * row_chunks;
+    int part;
+    if (d.partition_pages > 0) {
+        part = std::min(d.partition_pages, max_pages);
+    } else {
+        const int64_t target = 2LL * cu_count();
+        int64_t ns = (target + units - 1) / units;
+        const int64_t ns_cap = std::max<int64_t>(1, max_pages / (2 * kWaves));
+        ns = std::max<int64_t>(1, std::min(ns, ns_cap));
+        part = (int)((max_pages + ns - 1) / ns);
+    }
+    part = std::min(part, 64 * kWaves);        // each wave holds at most 64 page ids
+    const int64_t ns = (max_pages + part - 1) / part;
+    const int64_t grid = units * ns;
+    if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+    pl->partition_pages = part;
+    pl->num_splits = (int32_t)ns;
+    pl->row_tiles = nt;
+    pl->row_chunks = (int32_t)row_chunks;
+    pl->waves = kWaves;
+    pl->grid = (int32_t)grid;
+    pl->reduce = ns > 1 ? 1 : 0;
+    return PA_OK;
+}
+
+size_t workspace_for(const pa_plan& pl, int32_t batch, int32_t n, int32_t hq)
+{
+    if (!pl.reduce) return 0;
+    const size_t rows = (size_t)batch * n * hq * pl.num_splits;
+    const size_t acc = rows * kHeadDim * sizeof(float);
+    const size_t acc_aligned = (acc + 255) & ~size_t(255);
+    return acc_aligned + rows * 2 * sizeof(float);
+}
+
+template <int KV, int NT>
+void launch_partition(const Args& a, int grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((paged_attn_partition<KV, NT, kWaves, kPrefetch>), dim3(grid),
+                       dim3(kWaves * kWave), 0, st, a);
+}
+
+template <int KV>
+void launch_partition_nt(int nt, const Args& a, int grid, hipStream_t st)
+{
+    switch (nt) {
+    case 1: launch_partition<KV, 1>(a, grid, st); break;
+    case 2: launch_partition<KV, 2>(a, grid, st); break;
+    case 3: launch_partition<KV, 3>(a, grid, st); break;
+    default: launch_partition<KV, 4>(a, grid, st); break;
+    }
+}
+
+pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+              const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+              int32_t max_seq_len, int32_t batch, int32_t n, int32_t hq, float scale,
+              void* workspace, size_t workspace_bytes, void* stream, void* ev_begin,
+              void* ev_end)
+{
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "null pool");
+    if (!q || !out || !block_table || !seq_lens)
+        return fail(PA_ERR_INVALID_ARG, "null q, out, block_table or seq_lens");
+    const pa_pool_desc& d = pool->d;
+    const bool combo_ok = (d.kv_dtype == PA_F32 && q_dtype == PA_F32) ||
+                          (d.kv_dtype == PA_BF16 && q_dtype == PA_BF16) ||
+                          (d.kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16);
+    if (!dtype_known(q_dtype)) return fail(PA_ERR_INVALID_ARG, "unknown q dtype");
+    if (!combo_ok)
+        return fail(PA_ERR_UNSUPPORTED,
+                    "supported (kv, q) dtypes: (f32, f32), (bf16, bf16), (fp8, bf16)");
+    if (max_pages_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+    if (max_seq_len > (int64_t)kPage * max_pages_per_seq)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_pages_per_seq");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    pa_plan pl;
+    pa_status stt = make_plan(pool, batch, n, hq, max_seq_len, &pl);
+    if (stt != PA_OK) return stt;
+    const size_t need = workspace_for(pl, batch, n, hq);
+    if (need > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace required for a split call");
+        if (workspace_bytes < need) return fail(PA_ERR_WORKSPACE, "workspace too small");
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(d.k) % 16 ||
+        reinterpret_cast<uintptr_t>(d.v) % 16)
+        return fail(PA_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(out) % elem_size(q_dtype))
+        return fail(PA_ERR_INVALID_ARG, "out must be aligned to its element size");
+
+    Args a;
+    a.k = d.k;
+    a.v = d.v;
+    a.k_scale = d.k_scale;
+    a.v_scale = d.v_scale;
+    a.q = q;
+    a.out = out;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.part_acc = static_cast<float*>(workspace);
+    a.part_ml = need ? reinterpret_cast<float*>(
+                           static_cast<char*>(workspace) +
+                           (((size_t)batch * n * hq * pl.num_splits * kHeadDim * sizeof(float) +
+                             255) & ~size_t(255)))
+                     : nullptr;
+    a.page_stride = (int64_t)d.num_kv_heads * kSlab;
+    a.num_pages = d.num_pages;
+    a.max_pages = max_pages_per_seq;
+    a.n = n;
+    a.hq = hq;
+    a.hkv = d.num_kv_heads;
+    a.group = hq / d.num_kv_heads;
+    a.rows = a.group * n;
+    a.row_chunks = pl.row_chunks;
+    a.num_splits = pl.num_splits;
+    a.part_pages = pl.partition_pages;
+    a.scale_log2 = scale * kLog2e;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), st)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord(begin)");
+    switch (d.kv_dtype) {
+    case PA_F32: launch_partition_nt<KV_F32>(pl.row_tiles, a, pl.grid, st); break;
+    case PA_BF16: launch_partition_nt<KV_BF16>(pl.row_tiles, a, pl.grid, st); break;
+    default: launch_partition_nt<KV_FP8>(pl.row_tiles, a, pl.grid, st); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "partition kernel launch");
+    if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), st)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord(end)");
+    if (pl.reduce) {
+        const int64_t rows_out = (int64_t)batch * n * hq;
+        if (q_dtype == PA_F32)
+            hipLaunchKernelGGL(paged_attn_reduce<float>, dim3((unsigned)rows_out), dim3(kWave), 0,
+                               st, a);
+        else
+            hipLaunchKernelGGL(paged_attn_reduce<uint16_t>, dim3((unsigned)rows_out), dim3(kWave),
+                               0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "reduce kernel launch");
+    }
+    return PA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+PA_API pa_status paged_attn_pool_bytes(int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                                       int32_t head_dim, pa_dtype kv_dtype, size_t* k_bytes,
+                                       size_t* v_bytes)
+{
+    if (!k_bytes || !v_bytes) return fail(PA_ERR_INVALID_ARG, "null output pointer");
+    if (num_pages < 1 || page_size < 1 || num_kv_heads < 1 || head_dim < 1)
+        return fail(PA_ERR_INVALID_ARG, "counts must be >= 1");
+    if (!dtype_known(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype");
+    const size_t b = (size_t)num_pages * num_kv_heads * page_size * head_dim * elem_size(kv_dtype);
+    *k_bytes = b;
+    *v_bytes = b;
+    return PA_OK;
+}
+
+PA_API pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out)
+{
+    if (!out) return fail(PA_ERR_INVALID_ARG, "null output handle");
+    *out = nullptr;
+    if (!desc) return fail(PA_ERR_INVALID_ARG, "null descriptor");
+    if (desc->num_pages < 1 || desc->num_kv_heads < 1)
+        return fail(PA_ERR_INVALID_ARG, "num_pages and num_kv_heads must be >= 1");
+    if (!desc->k || !desc->v) return fail(PA_ERR_INVALID_ARG, "null k or v pool");
+    if (desc->page_size != kPage) return fail(PA_ERR_UNSUPPORTED, "page_size must be 16");
+    if (desc->head_dim != kHeadDim) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+    if (!dtype_known(desc->kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype");
+    if (desc->kv_dtype == PA_FP8_E4M3 && (!desc->k_scale || !desc->v_scale))
+        return fail(PA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
+    if (desc->partition_pages < 0) return fail(PA_ERR_INVALID_ARG, "partition_pages must be >= 0");
+    pa_pool* p = new (std::nothrow) pa_pool;
+    if (!p) return fail(PA_ERR_INVALID_ARG, "out of host memory");
+    p->d = *desc;
+    *out = p;
+    return PA_OK;
+}
+
+PA_API void paged_attn_destroy_pool(pa_pool* pool) { delete pool; }
+
+PA_API pa_status paged_attn_plan(const pa_pool* pool, int32_t batch, int32_t q_per_seq,
+                                 int32_t num_q_heads, int32_t max_seq_len, pa_plan* plan)
+{
+    return make_plan(pool, batch, q_per_seq, num_q_heads, max_seq_len, plan);
+}
+
+PA_API pa_status paged_attn_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t q_per_seq,
+                                            int32_t num_q_heads, int32_t max_seq_len,
+                                            size_t* bytes)
+{
+    if (!bytes) return fail(PA_ERR_INVALID_ARG, "null output pointer");
+    pa_plan pl;
+    pa_status st = make_plan(pool, batch, q_per_seq, num_q_heads, max_seq_len, &pl);
+    if (st != PA_OK) return st;
+    *bytes = workspace_for(pl, batch, q_per_seq, num_q_heads);
+    return PA_OK;
+}
+
+PA_API pa_status paged_attn_decode(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                                   const int32_t* block_table, int32_t max_pages_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                   int32_t num_q_heads, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
+               1, num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+PA_API pa_status paged_attn_verify(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                                   const int32_t* block_table, int32_t max_pages_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len, int32_t batch,
+                                   int32_t q_per_seq, int32_t num_q_heads, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
+               q_per_seq, num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+PA_API pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                                         void* out, const int32_t* block_table,
+                                         int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                         int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                         int32_t num_q_heads, float scale, void* workspace,
+                                         size_t workspace_bytes, void* stream, void* ev_begin,
+                                         void* ev_end)
+{
+    return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
+               q_per_seq, num_q_heads, scale, workspace, workspace_bytes, stream, ev_begin, ev_end);
+}
+
+PA_API pa_status paged_attn_validate(const pa_pool* pool, const int32_t* block_table,
+                                     int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                     int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                     void* stream)
+{
+    if (!pool || !block_table || !seq_lens) return fail(PA_ERR_INVALID_ARG, "null argument");
+    if (batch < 1 || max_pages_per_seq < 1 || q_per_seq < 1)
+        return fail(PA_ERR_INVALID_ARG, "counts must be >= 1");
+    std::vector<int32_t> lens(batch), tab((size_t)batch * max_pages_per_seq);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = hipMemcpyAsync(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, st)) !=
+        hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(seq_lens)");
+    if ((e = hipMemcpyAsync(tab.data(), block_table, tab.size() * 4, hipMemcpyDeviceToHost, st)) !=
+        hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(block_table)");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    for (int b = 0; b < batch; ++b) {
+        const int L = lens[b];
+        if (L < q_per_seq || L > max_seq_len || L > (int64_t)kPage * max_pages_per_seq) {
+            char msg[128];
+            snprintf(msg, sizeof msg, "seq_lens[%d] = %d out of range", b, L);
+            return fail(PA_ERR_CONTRACT, msg);
+        }
+        const int np = (L + kPage - 1) / kPage;
+        for (int p = 0; p < np; ++p) {
+            const int id = tab[(size_t)b * max_pages_per_seq + p];
+            if (id < 0 || id >= pool->d.num_pages) {
+                char msg[128];
+                snprintf(msg, sizeof msg, "block_table[%d][%d] = %d out of range", b, p, id);
+                return fail(PA_ERR_CONTRACT, msg);
+            }
+        }
+    }
+    return PA_OK;
+}
+
+PA_API const char* paged_attn_status_str(pa_status status)
+{
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_CONTRACT: return "device array violates the contract";
+    default: return "unknown status";
+    }
+}
+
+PA_API const char* paged_attn_last_error(void) { return g_last_error.c_str(); }

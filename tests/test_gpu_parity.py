@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Gates (max |GPU - oracle| over every compared output): 1e-5 for fp32 inputs,
+1.5e-2 for bf16 inputs with fp32 accumulation, 5e-2 for fp8-e4m3 KV; plus a
+relative L2 gate, because with N(0, 1) data the outputs shrink like
+sqrt(e / L) and a max-abs gate alone gets loose at long contexts.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from workloads.device import to_device, to_numpy_f64
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 5e-2}
+REL_L2 = {"f32": 1e-5, "bf16": 1e-2, "fp8": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import paged_kv_gqa_02_amd as lib
+    return lib
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(pa, case, partition_pages=0, dev=None, label=""):
+    say(f"[gpu] {case.name} {label} kv={case.kv_dtype} B={case.batch} n={case.q_per_seq} "
+        f"Hq={case.num_q_heads} Hkv={case.num_kv_heads} maxL={case.max_seq_len} "
+        f"part={partition_pages} seed={case.seed}")
+    d = dev if dev is not None else to_device(case)
+    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale, partition_pages)
+    out = torch.empty_like(d.q)
+    ws = pa.workspace_for(pool, d.q, case.max_seq_len)
+    pa.paged_attn_verify(pool, d.q, out, d.block_table, d.seq_lens, case.max_seq_len,
+                         case.scale, ws)
+    torch.cuda.synchronize()
+    return to_numpy_f64(out)
+
+
+def run_oracle(case, seqs=None):
+    return oracle.paged_attention(case.k_pool, case.v_pool, case.kv_dtype, case.q, case.q_dtype,
+                                  case.block_table, case.seq_lens, case.q_per_seq, case.scale,
+                                  seqs=seqs, k_scale=case.k_scale, v_scale=case.v_scale)
+
+
+def check(gpu, ref, kv_dtype, what):
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    err = float(np.abs(gpu - ref).max())
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+    say(f"    {what}: max_abs={err:.3e} rel_l2={rel:.3e}")
+    assert err <= MAX_ABS[kv_dtype], f"{what}: max abs error {err}"
+    assert rel <= REL_L2[kv_dtype], f"{what}: relative L2 error {rel}"
+    return err, rel
+
+
+def small_case(kv, n, hq, hkv, lens, seed, layout="shuffled", extra=3):
+    qd = "f32" if kv == "f32" else "bf16"
+    need = sum(W.pages_for(x) for x in lens)
+    kw = {} if layout == "fragmented" else {"num_pages": need + extra}
+    return W.make_case(f"small-{kv}", batch=len(lens), q_per_seq=n, num_q_heads=hq,
+                       num_kv_heads=hkv, seq_lens=lens, kv_dtype=kv, q_dtype=qd, seed=seed,
+                       layout=layout, **kw)
+
+
+# ----------------------------------------------------------------------------
+# small cases: every dtype, head layout, row count and split size
+# ----------------------------------------------------------------------------
+def test_tiny_workload(pa):
+    case = W.workload("tiny")
+    ref = run_oracle(case)
+    for part in (0, 1, 2, 3):
+        check(run_gpu(pa, case, part), ref, "f32", f"tiny part={part}")
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("n", [1, 5])
+@pytest.mark.parametrize("heads", [(8, 2), (4, 4), (8, 1), (16, 2)])
+def test_small_cases(pa, kv, n, heads):
+    hq, hkv = heads
+    lens = [max(n, 1), 17, 100, 333, 16, 48 + n]
+    case = small_case(kv, n, hq, hkv, lens, seed=1000 + 7 * n + hq + 3 * hkv)
+    ref = run_oracle(case)
+    dev = to_device(case)
+    for part in (0, 1, 3, 8):
+        check(run_gpu(pa, case, part, dev=dev), ref, kv, f"part={part}")
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_many_rows_span_several_workgroups(pa, kv):
+    # G = 8, n = 12 -> 96 rows: two row chunks of 64
+    case = small_case(kv, 12, 16, 2, [40, 200, 12], seed=77)
+    ref = run_oracle(case)
+    dev = to_device(case)
+    for part in (0, 2):
+        check(run_gpu(pa, case, part, dev=dev), ref, kv, f"rows=96 part={part}")
+
+
+def test_fragmented_pool(pa):
+    lens = W.ragged_lengths(np.random.default_rng(5), 24)
+    case = small_case("bf16", 1, 32, 8, lens, seed=55, layout="fragmented")
+    check(run_gpu(pa, case), run_oracle(case), "bf16", "fragmented")
+
+
+# ----------------------------------------------------------------------------
+# exactness checks with closed forms
+# ----------------------------------------------------------------------------
+def test_fp8_bytes_decode_exactly(pa):
+    """Single visible key: the output is that key's value row, for every finite byte."""
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+    case = small_case("fp8", 1, 4, 2, [1, 1], seed=3, extra=0)
+    vals = np.resize(finite, (2, 2, 128))                   # [seq][kv head][d]
+    vscale = np.float32(0.5)
+    for b in range(2):
+        page = case.block_table[b, 0]
+        case.v_pool[page, :, 0, :] = vals[b]
+        case.v_scale[page, :] = vscale
+    gpu = run_gpu(pa, case)
+    dec = np.vectorize(oracle.e4m3_value)(vals) * float(vscale)
+    for b in range(2):
+        for h in range(4):
+            assert (gpu[b, 0, h] == dec[b, h // 2]).all()
+
+
+def one_hot(case, rng):
+    """Make key j* of every (sequence, kv head) dominate: the output becomes V[j*]."""
+    g = case.num_q_heads // case.num_kv_heads
+    d = case.head_dim
+    u = rng.standard_normal((case.batch, case.num_kv_heads, d)).astype(np.float32)
+    u = np.round(u * 8) / 8                                  # exact in bf16 and e4m3
+    q = np.repeat(u[:, None, :, None, :], g, axis=3).reshape(case.batch, 1, case.num_q_heads, d)
+    q = np.broadcast_to(q, case.q.shape).astype(np.float32)
+    case.q = W.bf16_bits(q) if case.q_dtype == "bf16" else q
+    jstar = []
+    lam_min = (30 + math.log(case.max_seq_len)) * 2
+    for b in range(case.batch):
+        L = int(case.seq_lens[b])
+        js = rng.integers(0, L - case.q_per_seq + 1, size=case.num_kv_heads)
+        jstar.append(js)
+        for kh in range(case.num_kv_heads):
+            uu = float(u[b, kh] @ u[b, kh])
+            lam = lam_min / (case.scale * uu)
+            pages = case.block_table[b, :W.pages_for(L)]
+            if case.kv_dtype == "bf16":
+                case.k_pool[pages, kh, :, :] = 0
+            elif case.kv_dtype == "fp8":
+                case.k_pool[pages, kh, :, :] = 0
+                case.k_scale[pages, kh] = 1.0
+            else:
+                case.k_pool[pages, kh, :, :] = 0.0
+            p, slot = pages[js[kh] // 16], js[kh] % 16
+            row = (lam * u[b, kh]).astype(np.float32)
+            if case.kv_dtype == "bf16":
+                case.k_pool[p, kh, slot] = W.bf16_bits(row)
+            elif case.kv_dtype == "fp8":
+                case.k_pool[p, kh, slot] = W.e4m3_bytes(row)
+            else:
+                case.k_pool[p, kh, slot] = row
+    return jstar
+
+
+def check_one_hot(pa, case, label):
+    """Outputs are O(1) here, so the dtype gates are tight relative to them."""
+    rng = np.random.default_rng(case.seed + 1)
+    jstar = one_hot(case, rng)
+    gpu = run_gpu(pa, case, label=label + " one-hot")
+    seqs = [0, case.batch - 1]
+    check(gpu[seqs], run_oracle(case, seqs), case.kv_dtype, f"{label} one-hot vs oracle")
+    g = case.num_q_heads // case.num_kv_heads
+    for b in seqs:
+        for kh in range(case.num_kv_heads):
+            j = int(jstar[b][kh])
+            page, slot = case.block_table[b, j // 16], j % 16
+            raw = case.v_pool[page, kh, slot]
+            if case.kv_dtype == "bf16":
+                vrow = (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            elif case.kv_dtype == "fp8":
+                vrow = np.vectorize(oracle.e4m3_value)(raw) * float(case.v_scale[page, kh])
+            else:
+                vrow = raw.astype(np.float64)
+            got = gpu[b, :, kh * g:(kh + 1) * g]
+            err = np.abs(got - vrow).max()
+            assert err <= MAX_ABS[case.kv_dtype], f"{label}: b={b} kh={kh} off by {err}"
+
+
+# ----------------------------------------------------------------------------
+# invariants of the paged gather
+# ----------------------------------------------------------------------------
+def test_page_permutation_is_bitwise_invariant(pa):
+    case = small_case("bf16", 3, 8, 2, [30, 129, 64, 7], seed=91, extra=10)
+    base = run_gpu(pa, case, 2)
+    perm = np.random.default_rng(92).permutation(case.num_pages)
+    moved = W.Case(**{**case.__dict__})
+    moved.k_pool = np.empty_like(case.k_pool)
+    moved.v_pool = np.empty_like(case.v_pool)
+    moved.k_pool[perm] = case.k_pool
+    moved.v_pool[perm] = case.v_pool
+    moved.block_table = np.where(case.block_table >= 0,
+                                 perm[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+    assert (run_gpu(pa, moved, 2, label="permuted") == base).all()
+
+
+def test_repeat_calls_are_bitwise_identical(pa):
+    case = small_case("bf16", 1, 32, 8, [2048, 999], seed=93)
+    dev = to_device(case)
+    a = run_gpu(pa, case, dev=dev)
+    b = run_gpu(pa, case, dev=dev)
+    assert (a == b).all()
+
+
+def test_aliased_pages_give_identical_rows(pa):
+    case = small_case("bf16", 2, 8, 2, [70, 70, 33], seed=94)
+    case.block_table[1] = case.block_table[0]
+    case.q[1] = case.q[0]
+    out = run_gpu(pa, case, 1)
+    assert (out[0] == out[1]).all()
+    check(out, run_oracle(case), "bf16", "aliased")
+
+
+def test_verify_rows_match_prefix_decode(pa):
+    n = 5
+    case = small_case("bf16", n, 32, 8, [4101, 700, 90], seed=95)
+    ver = run_gpu(pa, case)
+    for i in range(n):
+        pref = W.Case(**{**case.__dict__})
+        pref.q_per_seq = 1
+        pref.q = np.ascontiguousarray(case.q[:, i:i + 1])
+        pref.seq_lens = (case.seq_lens - n + i + 1).astype(np.int32)
+        dec = run_gpu(pa, pref, label=f"prefix row {i}")
+        check(ver[:, i:i + 1], dec, "bf16", f"verify row {i} vs decode")
+
+
+def test_split_sizes_agree(pa):
+    case = small_case("f32", 5, 32, 8, [1000, 257, 5], seed=96)
+    dev = to_device(case)
+    ref = run_gpu(pa, case, 0, dev=dev)
+    for part in (1, 2, 5, 16, 63):
+        check(run_gpu(pa, case, part, dev=dev), ref, "f32", f"part={part} vs auto")
+
+
+def test_decode_entry_point_matches_verify(pa):
+    case = small_case("bf16", 1, 32, 8, [300, 2048, 17], seed=97)
+    d = to_device(case)
+    pool = pa.paged_attn_create_pool(d.k, d.v)
+    o1 = torch.empty_like(d.q)
+    o2 = torch.empty_like(d.q)
+    ws = pa.workspace_for(pool, d.q, case.max_seq_len)
+    pa.paged_attn_decode(pool, d.q, o1, d.block_table, d.seq_lens, case.max_seq_len,
+                         case.scale, ws)
+    pa.paged_attn_verify(pool, d.q, o2, d.block_table, d.seq_lens, case.max_seq_len,
+                         case.scale, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_validate_reports_bad_tables(pa):
+    case = small_case("bf16", 1, 8, 2, [40, 20], seed=98)
+    d = to_device(case)
+    pool = pa.paged_attn_create_pool(d.k, d.v)
+    pa.paged_attn_validate(pool, d.block_table, d.seq_lens, case.max_seq_len, 1)
+    bad = d.block_table.clone()
+    bad[1, 0] = case.num_pages
+    with pytest.raises(pa.PagedAttnError):
+        pa.paged_attn_validate(pool, bad, d.seq_lens, case.max_seq_len, 1)
+
+
+# ----------------------------------------------------------------------------
+# the named workloads at full size
+# ----------------------------------------------------------------------------
+def sampled(case):
+    idx = {0, case.batch - 1, int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))}
+    idx |= set(np.random.default_rng(case.seed).choice(case.batch, 2, replace=False).tolist())
+    return sorted(idx)
+
+
+@pytest.mark.parametrize("name", ["decode8b", "ragged", "verify", "fp8long"])
+def test_workload_native_dtype(pa, name):
+    case = W.workload(name)
+    gpu = run_gpu(pa, case)
+    seqs = sampled(case)
+    check(gpu[seqs], run_oracle(case, seqs), case.kv_dtype, f"{name} sampled {seqs}")
+
+
+@pytest.mark.parametrize("name", ["decode8b", "ragged", "verify", "fp8long"])
+def test_workload_fp32_structure(pa, name):
+    """Same shapes and layout in fp32: pins gather, masks and splits at 1e-5."""
+    case = W.workload(name, kv_dtype="f32", q_dtype="f32")
+    gpu = run_gpu(pa, case, label="fp32")
+    seqs = sampled(case)
+    check(gpu[seqs], run_oracle(case, seqs), "f32", f"{name} fp32 sampled {seqs}")
+
+
+@pytest.mark.parametrize("name", ["decode8b", "verify", "fp8long"])
+def test_workload_one_hot(pa, name):
+    case = W.workload(name, poison=True)
+    check_one_hot(pa, case, name)

@@ -88,20 +88,43 @@ def test_e4m3_encoder_ties_to_even_and_saturates():
     assert W.e4m3_bytes(np.array([-1e9]))[0] == 0xFE
 
 
-def test_e4m3_encoder_matches_torch_in_range():
-    x = _rng(1).standard_normal(200000) * 60
-    x = np.clip(x, -448, 448)
-    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    assert (W.e4m3_bytes(x) == ref).all()
+def _e4m3_table():
+    codes = np.array([b for b in range(256) if b not in (0x7F, 0xFF)])
+    return codes, np.array([oracle.e4m3_value(int(b)) for b in codes])
 
 
-def test_bf16_rounding_matches_torch():
+def test_e4m3_encoder_is_nearest_value_ties_to_even():
+    # brute force: the encoded byte decodes to the finite E4M3 value nearest x;
+    # on an exact tie the even code wins
+    codes, vals = _e4m3_table()
+    x = np.concatenate([_rng(1).standard_normal(20000) * 60,
+                        _rng(2).standard_normal(5000) * 0.01,
+                        (vals[1:] + vals[:-1]) / 2])               # every midpoint
+    x = x[np.abs(x) <= 448]
+    enc = W.e4m3_bytes(x)
+    dec = np.array([oracle.e4m3_value(int(b)) for b in enc])
+    dist = np.abs(x[:, None] - vals[None, :])
+    best = dist.min(axis=1)
+    assert (np.abs(x - dec) == best).all()
+    tie = (dist == best[:, None]).sum(axis=1) > 1
+    tie_codes = enc[tie]
+    nonzero = np.array([oracle.e4m3_value(int(b)) != 0 for b in tie_codes])
+    assert (tie_codes[nonzero] % 2 == 0).all()
+
+
+def test_bf16_rounding_is_nearest_ties_to_even():
     x = _rng(2).standard_normal(200000).astype(np.float32)
-    # exact ties: low half 0x8000 with both parities of the kept lsb
     ties = np.array([0x3F808000, 0x3F818000, 0xBF808000], dtype=np.uint32).view(np.float32)
-    x = np.concatenate([x, ties])
-    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    assert (W.bf16_bits(x) == ref).all()
+    bits = W.bf16_bits(np.concatenate([x, ties]))
+    dec = np.array([oracle.bf16_value(int(b)) for b in bits[-3:]])
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: the even pattern 0x3F80 wins
+    assert list(bits[-3:]) == [0x3F80, 0x3F82, 0xBF80]
+    assert dec[0] == 1.0
+    # every other value is within half a bf16 ulp
+    vals = (bits[:-3].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(x))[1] - 8)
+    assert (np.abs(vals - x) <= ulp / 2).all()
+    assert (W.bf16_bits(np.array([np.nan], dtype=np.float32)) == 0x7FC0).all()
 
 
 # ----------------------------------------------------------------------------

@@ -31,6 +31,7 @@ import math
 from typing import Optional
 
 import numpy as np
+import torch
 
 PAGE_SIZE = 16
 HEAD_DIM = 128
@@ -45,14 +46,13 @@ E4M3_NAN = np.uint8(0x7F)
 # storage-format rounding (input preparation only)
 # ----------------------------------------------------------------------------
 def bf16_bits(x) -> np.ndarray:
-    """Round float32 values to bfloat16 (round to nearest, ties to even).
+    """Round to bfloat16 (round to nearest, ties to even); the 16-bit patterns as uint16.
 
-    Returns the 16-bit patterns as uint16.  NaN stays NaN.
+    NaN becomes the canonical quiet NaN 0x7FC0.
     """
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    r = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    r = r.copy()
     nan = np.isnan(f)
     if nan.any():
         r[nan] = BF16_NAN
@@ -60,39 +60,21 @@ def bf16_bits(x) -> np.ndarray:
 
 
 def e4m3_bytes(x) -> np.ndarray:
-    """Encode values as OCP E4M3 bytes: round to nearest even, saturate at 448.
+    """Encode as OCP E4M3 bytes: round to nearest even, saturate at +-448, NaN -> 0x7F.
 
     E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
-    holds subnormals m/8 * 2^-6; 0x7F / 0xFF are NaN; the largest finite
-    magnitude is 448 (code 0x7E).  Works in chunks to bound host memory.
+    holds subnormals m/8 * 2^-6; S.1111.111 is NaN; the largest finite
+    magnitude is 448 (code 0x7E).
     """
-    x = np.asarray(x)
-    flat = x.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    step = 1 << 22
-    for s in range(0, flat.size, step):
-        out[s:s + step] = _e4m3_chunk(flat[s:s + step].astype(np.float64))
-    return out.reshape(x.shape)
-
-
-def _e4m3_chunk(x: np.ndarray) -> np.ndarray:
-    a = np.abs(x)
-    code = np.zeros(a.shape, dtype=np.int64)
-    sub = a < 2.0 ** -6
-    # subnormal range: steps of 2^-9; rounding up to 8 lands on the first normal (code 8)
-    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)
-    norm = ~sub & np.isfinite(a)
-    if norm.any():
-        an = a[norm]
-        _, ex = np.frexp(an)               # an = f * 2^ex, f in [0.5, 1)
-        e = ex.astype(np.int64) - 1         # an in [2^e, 2^(e+1))
-        steps = np.rint(an / np.ldexp(1.0, e - 3)).astype(np.int64)  # in [8, 16]
-        code[norm] = ((e + 7) << 3) + (steps - 8)   # carry 16 -> next binade
-    code = np.minimum(code, 0x7E)           # saturate (also catches +inf)
-    out = code.astype(np.uint8)
-    out[np.signbit(x)] |= np.uint8(0x80)
-    out[np.isnan(x)] = E4M3_NAN
-    return out
+    a = np.asarray(x)
+    if a.dtype not in (np.float32, np.float64):
+        a = a.astype(np.float64)
+    a = np.ascontiguousarray(np.clip(a, -E4M3_MAX, E4M3_MAX))
+    r = torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = E4M3_NAN
+    return r
 
 
 def pages_for(length: int) -> int:

@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=5)
     return ap.parse_args()
 
 

@@ -4,8 +4,10 @@ Default: the 8B-GQA decode layer (batch 64, one query row, 32 query heads / 8
 KV heads, head_dim 128, context 2048, page size 16, bf16 K/V/Q, block tables
 from a seeded shuffled free list).  One step = one paged_attn_verify call
 (partition kernel, plus the split-K reduce when the plan splits) over the
-whole batch; inputs are resident in HBM and a 1 GiB buffer is overwritten
-before every step so that no K/V byte is served from L2 or the MALL.
+whole batch; inputs are resident in HBM and a 1 GiB buffer is read before
+every step so that no K/V byte is served from L2 or the MALL.  The flush
+reads rather than writes: a written buffer leaves dirty lines in the MALL
+whose write-back would then compete with the timed kernel for HBM.
 
 Prints ONE JSON line (rank 0).  `value` is effective HBM GB/s: (K + V bytes of
 every token of every sequence, fp8 scales, Q, O) / mean call time.
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a torch copy of 512 MiB ten times (scale for HBM counters)")
     return ap.parse_args()
 
 
@@ -72,6 +76,18 @@ def cpu_baseline(case, reps):
             "tokens_per_s": case.batch * case.q_per_seq / t}
 
 
+def copy_calibration(torch):
+    """A plain device copy of known size: reads and writes 512 MiB per launch."""
+    n = 512 << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(10):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 10}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -86,6 +102,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     log(f"generating {args.workload}")
     case = W.workload(args.workload)
@@ -96,18 +115,21 @@ def main():
                               case.max_seq_len)
     out = torch.empty_like(dev.q)
     ws = pa.workspace_for(pool, dev.q, case.max_seq_len)
-    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = None
+    if not args.no_flush:
+        flush = torch.ones(FLUSH_BYTES // 2, dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(evs=None):
         if flush is not None:
-            flush.fill_(1)
+            flush.sum(dtype=torch.float32)
         if evs is None:
             pa.paged_attn_verify(pool, dev.q, out, dev.block_table, dev.seq_lens,
                                  case.max_seq_len, case.scale, ws)
         else:
-            c0, k0, k1, c1 = evs
-            c0.record(stream)
+            # k0: right before the partition kernel (= start of the call),
+            # k1: right after it, c1: after the whole call (reduce included)
+            k0, k1, c1 = evs
             pa.paged_attn_verify(pool, dev.q, out, dev.block_table, dev.seq_lens,
                                  case.max_seq_len, case.scale, ws, ev_begin=k0, ev_end=k1)
             c1.record(stream)
@@ -117,15 +139,15 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[pa.HipEvent() for _ in range(4)] for _ in range(args.steps)]
+    evs = [[pa.HipEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = np.array([e[0].elapsed_ms(e[3]) for e in evs])
-    kern_ms = np.array([e[1].elapsed_ms(e[2]) for e in evs])
+    call_ms = np.array([e[0].elapsed_ms(e[2]) for e in evs])
+    kern_ms = np.array([e[0].elapsed_ms(e[1]) for e in evs])
     log(f"timed {args.steps} steps: call {call_ms.mean() * 1e3:.1f} us, "
         f"partition kernel {kern_ms.mean() * 1e3:.1f} us")
 

@@ -42,6 +42,8 @@ class pa_pool_desc(ctypes.Structure):
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
         ("partition_pages", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
+        ("prefetch", ctypes.c_int32),
     ]
 
 
@@ -167,14 +169,14 @@ def paged_attn_pool_bytes(num_pages: int, num_kv_heads: int, kv_dtype: int,
 
 
 def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None,
-                           partition_pages: int = 0) -> Pool:
+                           partition_pages: int = 0, waves: int = 0, prefetch: int = 0) -> Pool:
     """k, v: [num_pages][Hkv][16][128] device tensors (float32, bfloat16 or fp8 bytes)."""
     if k.shape != v.shape or k.dim() != 4:
         raise ValueError("k and v must both be [num_pages][Hkv][16][128]")
     desc = pa_pool_desc(num_pages=k.shape[0], page_size=k.shape[2], num_kv_heads=k.shape[1],
                         head_dim=k.shape[3], kv_dtype=_kv_code(k), k=_dptr(k), v=_dptr(v),
                         k_scale=_dptr(k_scale), v_scale=_dptr(v_scale),
-                        partition_pages=partition_pages)
+                        partition_pages=partition_pages, waves=waves, prefetch=prefetch)
     h = ctypes.c_void_p()
     _check(_lib.paged_attn_create_pool(ctypes.byref(desc), ctypes.byref(h)),
            "paged_attn_create_pool")

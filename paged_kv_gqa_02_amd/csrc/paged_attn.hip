@@ -109,6 +109,29 @@ __device__ __forceinline__ float fast_exp2(float x)
     return __builtin_amdgcn_exp2f(x);
 }
 
+// Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 lane-swap instructions: swapping a register with
+// itself leaves one copy of each partner value in the returned pair.
+__device__ __forceinline__ float group_max(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(y);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group_sum(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __float_as_uint(y);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Two E4M3 bytes (low or high half of w) -> two bf16 in one dword.  E4M3 is
 // a subset of bf16, so the conversion is exact.
 template <bool kHigh>
@@ -200,26 +223,30 @@ __device__ __forceinline__ void load_page(Page<KV_F32>& p, const Args& a, int ph
     }
 }
 
-// zero the V rows of tokens at or past the sequence end (their slots may hold NaN)
+// V rows of tokens at or past the sequence end (their slots may hold NaN) are
+// replaced by zeros once loaded; s counts this lane's tokens 4g + s
 __device__ __forceinline__ void clear_dead_v(Page<KV_BF16>& p, int first_dead_s)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        if (s >= first_dead_s) p.v[s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.v[s][e] = (s < first_dead_s) ? p.v[s][e] : 0u;
 }
 __device__ __forceinline__ void clear_dead_v(Page<KV_FP8>& p, int first_dead_s)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        if (s >= first_dead_s) p.v[s] = u32x2{0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) p.v[s][e] = (s < first_dead_s) ? p.v[s][e] : 0u;
 }
 __device__ __forceinline__ void clear_dead_v(Page<KV_F32>& p, int first_dead_s)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        if (s >= first_dead_s) {
-            p.v[2 * s] = f32x4{0.f, 0.f, 0.f, 0.f};
-            p.v[2 * s + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p.v[2 * s][e] = (s < first_dead_s) ? p.v[2 * s][e] : 0.f;
+            p.v[2 * s + 1][e] = (s < first_dead_s) ? p.v[2 * s + 1][e] : 0.f;
         }
 }
 
@@ -427,7 +454,6 @@ __global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
 
     auto consume = [&](Page<KV>& pg, int j) {
         const int base = (pg0 + wave + j * W) * kPage;
-        if (base + kPage > L) clear_dead_v(pg, (L - base - 4 * g));
         const bool need_mask = base + kPage - 1 > first_limit;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -440,9 +466,7 @@ __global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
                 for (int v = 0; v < 4; ++v)
                     s[v] = (base + 4 * g + v <= lim[nt]) ? s[v] : -INFINITY;
             }
-            float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = group_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
             const float mnew = fmaxf(m[nt], mx);
             const float alpha = fast_exp2(m[nt] - mnew);
             m[nt] = mnew;
@@ -451,34 +475,36 @@ __global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
             for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mnew);
 #pragma unroll
             for (int db = 0; db < 8; ++db) acc[nt].o[db] *= alpha;
+            if (nt == 0 && base + kPage > L) clear_dead_v(pg, L - base - 4 * g);
             l[nt] = l[nt] * alpha + pv(acc[nt], pg, p);
         }
     };
 
-    Page<KV> buf[PF];
+    // Software pipeline: page j + PF - 1 is requested before page j is used.
+    // Loads are unconditional (indices past the last page repeat the last
+    // page) so that the wait before each use covers only that page's loads.
+    if (nj > 0) {
+        auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(my_id, min(j, nj - 1)); };
+        Page<KV> buf[PF];
 #pragma unroll
-    for (int st = 0; st < PF - 1; ++st)
-        if (st < nj) load_page(buf[st], a, __builtin_amdgcn_readlane(my_id, st), kh, l16, g);
-
-    for (int j0 = 0; j0 < nj; j0 += PF) {
+        for (int st = 0; st < PF - 1; ++st) load_page(buf[st], a, phys_of(st), kh, l16, g);
+        int j0 = 0;
+        for (; j0 + PF <= nj; j0 += PF) {
 #pragma unroll
-        for (int st = 0; st < PF; ++st) {
-            const int j = j0 + st;
-            if (j < nj) {
-                const int jn = j + PF - 1;
-                if (jn < nj)
-                    load_page(buf[(st + PF - 1) % PF], a, __builtin_amdgcn_readlane(my_id, jn),
-                              kh, l16, g);
-                consume(buf[st], j);
+            for (int st = 0; st < PF; ++st) {
+                load_page(buf[(st + PF - 1) % PF], a, phys_of(j0 + st + PF - 1), kh, l16, g);
+                consume(buf[st], j0 + st);
             }
         }
+#pragma unroll
+        for (int st = 0; st < PF - 1; ++st)
+            if (j0 + st < nj) consume(buf[st], j0 + st);
     }
 
     // ---- merge the waves of this workgroup (fixed order) ----
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        l[nt] += __shfl_xor(l[nt], 16);
-        l[nt] += __shfl_xor(l[nt], 32);
+        l[nt] = group_sum(l[nt]);
         if (g == 0) {
             sm_ml[wave][nt * 16 + l16][0] = m[nt];
             sm_ml[wave][nt * 16 + l16][1] = l[nt];
@@ -616,8 +642,15 @@ int cu_count()
     return cache[dev];
 }
 
-constexpr int kWaves = 8;        // waves per workgroup of the partition kernel
-constexpr int kPrefetch = 2;     // pages held in registers per wave (1 in flight + 1 in use)
+// Defaults measured on MI355X (bf16 8B-GQA decode, B64 ctx 2048): four waves
+// per workgroup and a three-page register pipeline for one row tile; two
+// pages when the query tile (two row tiles, or fp8 conversion) needs the
+// registers.
+constexpr int kWaves = 4;
+constexpr int default_prefetch(pa_dtype kv, int row_tiles)
+{
+    return (row_tiles == 1 && kv != PA_FP8_E4M3) ? 3 : 2;
+}
 
 size_t elem_size(pa_dtype t)
 {
@@ -656,11 +689,13 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     } else {
         const int64_t target = 2LL * cu_count();
         int64_t ns = (target + units - 1) / units;
-        const int64_t ns_cap = std::max<int64_t>(1, max_pages / (2 * kWaves));
+        const int64_t ns_cap =
+            std::max<int64_t>(1, max_pages / (2 * (d.waves > 0 ? d.waves : kWaves)));
         ns = std::max<int64_t>(1, std::min(ns, ns_cap));
         part = (int)((max_pages + ns - 1) / ns);
     }
-    part = std::min(part, 64 * kWaves);        // each wave holds at most 64 page ids
+    const int waves = d.waves > 0 ? d.waves : kWaves;
+    part = std::min(part, 64 * waves);         // each wave holds at most 64 page ids
     const int64_t ns = (max_pages + part - 1) / part;
     const int64_t grid = units * ns;
     if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
@@ -668,7 +703,7 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     pl->num_splits = (int32_t)ns;
     pl->row_tiles = nt;
     pl->row_chunks = (int32_t)row_chunks;
-    pl->waves = kWaves;
+    pl->waves = waves;
     pl->grid = (int32_t)grid;
     pl->reduce = ns > 1 ? 1 : 0;
     return PA_OK;
@@ -683,21 +718,43 @@ size_t workspace_for(const pa_plan& pl, int32_t batch, int32_t n, int32_t hq)
     return acc_aligned + rows * 2 * sizeof(float);
 }
 
-template <int KV, int NT>
+template <int KV, int NT, int W, int PF>
 void launch_partition(const Args& a, int grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((paged_attn_partition<KV, NT, kWaves, kPrefetch>), dim3(grid),
-                       dim3(kWaves * kWave), 0, st, a);
+    hipLaunchKernelGGL((paged_attn_partition<KV, NT, W, PF>), dim3(grid), dim3(W * kWave), 0, st,
+                       a);
+}
+
+// (waves, prefetch) variants are instantiated for the bf16 and fp8 paths with
+// one or two row tiles; every other shape runs the default variant
+template <int KV, int NT>
+void launch_tuned(int waves, int prefetch, const Args& a, int grid, hipStream_t st)
+{
+    if (KV == KV_F32 || NT > 2) {
+        launch_partition<KV, NT, kWaves, 2>(a, grid, st);
+        return;
+    }
+    const int key = waves * 10 + prefetch;
+    switch (key) {
+    case 42: launch_partition<KV, NT, 4, 2>(a, grid, st); break;
+    case 43: launch_partition<KV, NT, 4, 3>(a, grid, st); break;
+    case 44: launch_partition<KV, NT, 4, 4>(a, grid, st); break;
+    case 83: launch_partition<KV, NT, 8, 3>(a, grid, st); break;
+    case 84: launch_partition<KV, NT, 8, 4>(a, grid, st); break;
+    case 82: launch_partition<KV, NT, 8, 2>(a, grid, st); break;
+    default: launch_partition<KV, NT, 4, 2>(a, grid, st); break;
+    }
 }
 
 template <int KV>
-void launch_partition_nt(int nt, const Args& a, int grid, hipStream_t st)
+void launch_partition_nt(int nt, int waves, int prefetch, const Args& a, int grid,
+                         hipStream_t st)
 {
     switch (nt) {
-    case 1: launch_partition<KV, 1>(a, grid, st); break;
-    case 2: launch_partition<KV, 2>(a, grid, st); break;
-    case 3: launch_partition<KV, 3>(a, grid, st); break;
-    default: launch_partition<KV, 4>(a, grid, st); break;
+    case 1: launch_tuned<KV, 1>(waves, prefetch, a, grid, st); break;
+    case 2: launch_tuned<KV, 2>(waves, prefetch, a, grid, st); break;
+    case 3: launch_tuned<KV, 3>(waves, prefetch, a, grid, st); break;
+    default: launch_tuned<KV, 4>(waves, prefetch, a, grid, st); break;
     }
 }
 
@@ -770,10 +827,11 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
     hipError_t e;
     if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), st)) != hipSuccess)
         return hip_fail(e, "hipEventRecord(begin)");
+    const int pf = d.prefetch > 0 ? d.prefetch : default_prefetch(d.kv_dtype, pl.row_tiles);
     switch (d.kv_dtype) {
-    case PA_F32: launch_partition_nt<KV_F32>(pl.row_tiles, a, pl.grid, st); break;
-    case PA_BF16: launch_partition_nt<KV_BF16>(pl.row_tiles, a, pl.grid, st); break;
-    default: launch_partition_nt<KV_FP8>(pl.row_tiles, a, pl.grid, st); break;
+    case PA_F32: launch_partition_nt<KV_F32>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
+    case PA_BF16: launch_partition_nt<KV_BF16>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
+    default: launch_partition_nt<KV_FP8>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "partition kernel launch");
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), st)) != hipSuccess)
@@ -824,6 +882,10 @@ PA_API pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out)
     if (desc->kv_dtype == PA_FP8_E4M3 && (!desc->k_scale || !desc->v_scale))
         return fail(PA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
     if (desc->partition_pages < 0) return fail(PA_ERR_INVALID_ARG, "partition_pages must be >= 0");
+    if (desc->waves != 0 && desc->waves != 4 && desc->waves != 8)
+        return fail(PA_ERR_UNSUPPORTED, "waves must be 0, 4 or 8");
+    if (desc->prefetch != 0 && (desc->prefetch < 2 || desc->prefetch > 4))
+        return fail(PA_ERR_UNSUPPORTED, "prefetch must be 0 or 2..4");
     pa_pool* p = new (std::nothrow) pa_pool;
     if (!p) return fail(PA_ERR_INVALID_ARG, "out of host memory");
     p->d = *desc;

@@ -33,7 +33,8 @@ def test_status_strings():
 
 def _desc(**kw):
     d = dict(num_pages=64, page_size=16, num_kv_heads=8, head_dim=128, kv_dtype=B.PA_BF16,
-             k=FAKE_K, v=FAKE_V, k_scale=None, v_scale=None, partition_pages=0)
+             k=FAKE_K, v=FAKE_V, k_scale=None, v_scale=None, partition_pages=0, waves=0,
+             prefetch=0)
     d.update(kw)
     return B.pa_pool_desc(**d)
 
@@ -53,6 +54,8 @@ def _create(**kw):
     (dict(k=None), B.PA_ERR_INVALID_ARG),
     (dict(kv_dtype=B.PA_FP8_E4M3), B.PA_ERR_INVALID_ARG),      # fp8 without scales
     (dict(partition_pages=-1), B.PA_ERR_INVALID_ARG),
+    (dict(waves=6), B.PA_ERR_UNSUPPORTED),
+    (dict(prefetch=9), B.PA_ERR_UNSUPPORTED),
 ])
 def test_create_pool_rejects(kw, status):
     st, h = _create(**kw)

@@ -33,12 +33,13 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_gpu(pa, case, partition_pages=0, dev=None, label=""):
+def run_gpu(pa, case, partition_pages=0, dev=None, label="", waves=0, prefetch=0):
     say(f"[gpu] {case.name} {label} kv={case.kv_dtype} B={case.batch} n={case.q_per_seq} "
         f"Hq={case.num_q_heads} Hkv={case.num_kv_heads} maxL={case.max_seq_len} "
-        f"part={partition_pages} seed={case.seed}")
+        f"part={partition_pages} waves={waves} prefetch={prefetch} seed={case.seed}")
     d = dev if dev is not None else to_device(case)
-    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale, partition_pages)
+    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale, partition_pages, waves,
+                                     prefetch)
     out = torch.empty_like(d.q)
     ws = pa.workspace_for(pool, d.q, case.max_seq_len)
     pa.paged_attn_verify(pool, d.q, out, d.block_table, d.seq_lens, case.max_seq_len,
@@ -103,6 +104,20 @@ def test_many_rows_span_several_workgroups(pa, kv):
     dev = to_device(case)
     for part in (0, 2):
         check(run_gpu(pa, case, part, dev=dev), ref, kv, f"rows=96 part={part}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("n", [1, 5])
+def test_tuning_variants(pa, kv, n):
+    """Every (waves, prefetch) instantiation, unsplit and split, against the oracle."""
+    case = small_case(kv, n, 32, 8, [513, 100, 17, 2048, 64], seed=31 + n)
+    ref = run_oracle(case)
+    dev = to_device(case)
+    for waves in (4, 8):
+        for prefetch in (2, 3, 4):
+            for part in (0, 7):
+                check(run_gpu(pa, case, part, dev=dev, waves=waves, prefetch=prefetch), ref, kv,
+                      f"waves={waves} prefetch={prefetch} part={part}")
 
 
 def test_fragmented_pool(pa):

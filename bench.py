@@ -48,6 +48,23 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the kernel source as it is now (else None)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "traffic.json")
+    src = os.path.join(root, "paged_kv_gqa_02_amd", "csrc", "paged_attn.hip")
+    try:
+        rec = json.load(open(path)).get(workload)
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != digest:
+        return None
+    return int(round(rec["traffic_bytes"]))
+
+
 def cpu_baseline(case, reps):
     """The float64 oracle, as it is, over the whole batch on every host core."""
     import concurrent.futures as cf
@@ -185,7 +202,8 @@ def main():
         "plan": plan,
         "roofline": {"bound": "hbm", "kernel": "paged_attn_partition",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(case.name),
                      "kernel_us_mean": round(kern_s * 1e6, 2),
                      "algorithmic_bytes_per_launch": nbytes},
     }

@@ -21,7 +21,14 @@
  *   "Latency and cost in production" §10.8.2-§10.8.3).
  *
  * Layouts (all row-major, all device memory unless noted):
- *   K pool, V pool   [num_pages][num_kv_heads][16][128] elements of kv_dtype
+ *   V pool           [num_pages][num_kv_heads][16][128] elements of kv_dtype
+ *                    (token-major: one 128-element row per token)
+ *   K pool           [num_pages][num_kv_heads][128 / x][16][x], x = 16 bytes /
+ *                    element size (4 for f32, 8 for bf16, 16 for fp8): the head
+ *                    dimension of a (page, head) slab is cut into 16-byte
+ *                    chunks and each chunk holds the 16 tokens one after
+ *                    another.  Element d of token t is at slab index
+ *                    ((d / x) * 16 + t) * x + d % x.
  *   k_scale, v_scale [num_pages][num_kv_heads] float32 (fp8 pools only)
  *   q, out           [batch][q_per_seq][num_q_heads][128] elements of q_dtype
  *                    (out has the dtype of q)
@@ -81,8 +88,8 @@ typedef struct pa_pool_desc {
     int32_t num_kv_heads;
     int32_t head_dim;         /* must be 128 */
     pa_dtype kv_dtype;
-    const void* k;            /* [num_pages][num_kv_heads][16][128] */
-    const void* v;            /* same layout as k */
+    const void* k;            /* [num_pages][num_kv_heads][128/x][16][x], x = 16 / elem size */
+    const void* v;            /* [num_pages][num_kv_heads][16][128] */
     const float* k_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
     const float* v_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
     int32_t partition_pages;  /* split-K partition length in pages; 0 = chosen per call */

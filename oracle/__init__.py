@@ -95,8 +95,10 @@ def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
                     k_scale=None, v_scale=None) -> np.ndarray:
     """Paged attention read straight from the pool, for the listed sequences.
 
-    k_pool / v_pool: [num_pages][Hkv][page_size][D] as float32 (``f32``),
-    uint16 bf16 bits (``bf16``) or uint8 E4M3 bytes (``fp8``).
+    v_pool: [num_pages][Hkv][page_size][D] as float32 (``f32``), uint16 bf16
+    bits (``bf16``) or uint8 E4M3 bytes (``fp8``); k_pool: the same elements in
+    the chunked K layout [num_pages][Hkv][D/x][page_size][x], x = 16 bytes /
+    element size.
     q: [batch][n][Hq][D] float32 or uint16 bf16 bits.  Returns
     [len(seqs)][n][Hq][D] float64.
     """
@@ -105,9 +107,11 @@ def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
     q = np.ascontiguousarray(q)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
-    num_pages, hkv, page_size, d = k_pool.shape
+    num_pages, hkv, page_size, d = v_pool.shape
     batch, n, hq, dq = q.shape
-    if n != q_per_seq or dq != d or v_pool.shape != k_pool.shape:
+    x = 16 // v_pool.dtype.itemsize
+    if (n != q_per_seq or dq != d or k_pool.dtype != v_pool.dtype
+            or k_pool.shape != (num_pages, hkv, d // x, page_size, x)):
         raise ValueError("shape mismatch")
     if bt.ndim != 2 or bt.shape[0] != batch or lens.shape != (batch,):
         raise ValueError("block_table / seq_lens must have one row per sequence")

@@ -86,6 +86,12 @@ int oracle_attention(const double* q, const double* k, const double* v,
     return ORACLE_OK;
 }
 
+/* bytes of one element of the given code */
+static int element_bytes(int code)
+{
+    return code == ORACLE_F32 ? 4 : code == ORACLE_BF16 ? 2 : 1;
+}
+
 /* value of element `idx` of an array of the given element code */
 static double element(const void* base, int code, size_t idx)
 {
@@ -121,6 +127,10 @@ int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
     if (num_pages < 1 || Hkv < 1 || page_size < 1 || D < 1 || max_pages < 1 ||
         batch < 1 || n < 1 || Hq < Hkv || Hq % Hkv != 0 || nseqs < 0)
         return ORACLE_BAD_ARG;
+    /* K slabs hold the head dimension in chunks of 16 bytes = x elements */
+    const int x = 16 / element_bytes(kv_dtype);
+    if (D % x != 0)
+        return ORACLE_BAD_ARG;
 
     for (int s = 0; s < nseqs; ++s) {
         const int b = seqs[s];
@@ -153,11 +163,13 @@ int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
                     ks = (double)k_scale[(size_t)page * Hkv + hk];
                     vs = (double)v_scale[(size_t)page * Hkv + hk];
                 }
-                const size_t src = (((size_t)page * Hkv + hk) * page_size + slot) * D;
+                const size_t slab = ((size_t)page * Hkv + hk) * page_size * D;
+                const size_t vrow = slab + (size_t)slot * D;
                 const size_t dst = ((size_t)t * Hkv + hk) * D;
                 for (int d = 0; d < D; ++d) {
-                    kc[dst + d] = element(k_pool, kv_dtype, src + d) * ks;
-                    vc[dst + d] = element(v_pool, kv_dtype, src + d) * vs;
+                    const size_t kidx = slab + ((size_t)(d / x) * page_size + slot) * x + d % x;
+                    kc[dst + d] = element(k_pool, kv_dtype, kidx) * ks;
+                    vc[dst + d] = element(v_pool, kv_dtype, vrow + d) * vs;
                 }
             }
         }

@@ -66,8 +66,12 @@ int oracle_attention(const double* q, const double* k, const double* v,
 
 /*
  * Paged attention for the listed sequences, read straight from the pool.
- *   k_pool, v_pool  [num_pages][Hkv][page_size][D] elements of kv_dtype
- *                   (float32, bfloat16 bits, or E4M3 bytes)
+ *   v_pool          [num_pages][Hkv][page_size][D] elements of kv_dtype
+ *                   (float32, bfloat16 bits, or E4M3 bytes), token-major
+ *   k_pool          [num_pages][Hkv][D / x][page_size][x] with x = 16 bytes /
+ *                   element size: the library's documented K layout, in which
+ *                   the head dimension of a slab is cut into 16-byte chunks
+ *                   that each hold every token of the page in turn
  *   k_scale,v_scale [num_pages][Hkv] float32, used only for E4M3
  *   q               [batch][n][Hq][D] elements of q_dtype (float32 or bf16)
  *   block_table     [batch][max_pages] int32

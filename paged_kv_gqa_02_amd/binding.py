@@ -170,17 +170,19 @@ def paged_attn_pool_bytes(num_pages: int, num_kv_heads: int, kv_dtype: int,
 
 def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None,
                            partition_pages: int = 0, waves: int = 0, prefetch: int = 0) -> Pool:
-    """k, v: [num_pages][Hkv][16][128] device tensors (float32, bfloat16 or fp8 bytes)."""
-    if k.shape != v.shape or k.dim() != 4:
-        raise ValueError("k and v must both be [num_pages][Hkv][16][128]")
-    desc = pa_pool_desc(num_pages=k.shape[0], page_size=k.shape[2], num_kv_heads=k.shape[1],
-                        head_dim=k.shape[3], kv_dtype=_kv_code(k), k=_dptr(k), v=_dptr(v),
+    """v: [num_pages][Hkv][16][128]; k: the same elements in the chunked K layout
+    [num_pages][Hkv][128/x][16][x], x = 16 bytes / element size (device tensors of
+    float32, bfloat16 or fp8 bytes)."""
+    if v.dim() != 4 or k.dtype != v.dtype or k.numel() != v.numel() or k.shape[:2] != v.shape[:2]:
+        raise ValueError("v must be [num_pages][Hkv][16][128] and k the same elements, chunked")
+    desc = pa_pool_desc(num_pages=v.shape[0], page_size=v.shape[2], num_kv_heads=v.shape[1],
+                        head_dim=v.shape[3], kv_dtype=_kv_code(k), k=_dptr(k), v=_dptr(v),
                         k_scale=_dptr(k_scale), v_scale=_dptr(v_scale),
                         partition_pages=partition_pages, waves=waves, prefetch=prefetch)
     h = ctypes.c_void_p()
     _check(_lib.paged_attn_create_pool(ctypes.byref(desc), ctypes.byref(h)),
            "paged_attn_create_pool")
-    return Pool(h, (k, v, k_scale, v_scale), k.shape[0], k.shape[1])
+    return Pool(h, (k, v, k_scale, v_scale), v.shape[0], v.shape[1])
 
 
 def paged_attn_destroy_pool(pool: Pool):

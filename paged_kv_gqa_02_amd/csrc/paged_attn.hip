@@ -17,9 +17,9 @@
 //    K dimension and the group's query rows as N (padded to 16 per tile), so
 //    the GQA group and the verify rows share each K/V fragment in registers.
 //    Pages are loaded straight from HBM into VGPRs in the MFMA operand
-//    layout: a K fragment is 16 rows x 64 contiguous bytes per instruction, a
-//    V fragment 4 full 256-byte rows; V is transposed in registers with
-//    v_perm.  The QK output layout is exactly the PV B-operand layout, so the
+//    layout with non-temporal loads: K pages are stored in 16-byte head-dim
+//    chunks so one K fragment is 1 KiB contiguous, a V fragment is 4 whole
+//    256-byte token rows; V is transposed in registers with v_perm.  The QK output layout is exactly the PV B-operand layout, so the
 //    probabilities never leave their lanes.
 //  * Online softmax in the log2 domain (scale * log2 e folded into the
 //    scores, v_exp_f32), running max reduced across the 4 lane groups with
@@ -155,7 +155,13 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
 // ---------------------------------------------------------------------------
 // one page of K and V for one kv head, in MFMA operand layout
 //   l16 = lane % 16, g = lane / 16
-//   K: lane holds token l16; V: lane holds tokens 4g..4g+3, dims 8*l16..+7
+//   K slab: 16-byte chunks of the head dimension, the 16 tokens of a chunk
+//   stored one after another; byte offset of (chunk q, token t) = (16 q + t) * 16.
+//   The lanes of one load instruction c read chunks 4c .. 4c+3 of every token:
+//   1 KiB contiguous, lane (l16, g) gets chunk 4c + g of token l16.
+//   V slab: token-major rows; lane (l16, g) reads 16 bytes of token 4g + s per
+//   instruction s, so one instruction covers four whole rows.
+//   Loads are non-temporal: every K/V byte is used once per call.
 // ---------------------------------------------------------------------------
 template <int KV> struct Page;
 
@@ -175,18 +181,30 @@ template <> struct Page<KV_F32> {
     f32x4 v[8];   // v[2s + h]: V[4g + s][8 l16 + 4h .. +4]
 };
 
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
+// chunk (4c + g) of token l16: byte offset ((4c + g) * 16 + l16) * 16 = 1024 c + lane * 16
+__device__ __forceinline__ const u32x4* k_fragment(const void* slab, int lane)
+{
+    return reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(slab) + 16 * lane);
+}
+
 __device__ __forceinline__ void load_page(Page<KV_BF16>& p, const Args& a, int phys, int kh,
                                           int l16, int g)
 {
     const int64_t off = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
     const uint16_t* kb = static_cast<const uint16_t*>(a.k) + off;
     const uint16_t* vb = static_cast<const uint16_t*>(a.v) + off;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kb + l16 * kHeadDim + 8 * g);
+    const u32x4* kp = k_fragment(kb, 16 * g + l16);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb + 4 * g * kHeadDim + 8 * l16);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) p.k[c] = kp[4 * c];
+    for (int c = 0; c < 4; ++c) p.k[c] = stream_load(kp + 64 * c);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) p.v[s] = vp[16 * s];
+    for (int s = 0; s < 4; ++s) p.v[s] = stream_load(vp + 16 * s);
 }
 
 __device__ __forceinline__ void load_page(Page<KV_FP8>& p, const Args& a, int phys, int kh,
@@ -195,12 +213,12 @@ __device__ __forceinline__ void load_page(Page<KV_FP8>& p, const Args& a, int ph
     const int64_t off = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
     const uint8_t* kb = static_cast<const uint8_t*>(a.k) + off;
     const uint8_t* vb = static_cast<const uint8_t*>(a.v) + off;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kb + l16 * kHeadDim + 16 * g);
+    const u32x4* kp = k_fragment(kb, 16 * g + l16);
     const u32x2* vp = reinterpret_cast<const u32x2*>(vb + 4 * g * kHeadDim + 8 * l16);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) p.k[h] = kp[4 * h];
+    for (int h = 0; h < 2; ++h) p.k[h] = stream_load(kp + 64 * h);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) p.v[s] = vp[16 * s];
+    for (int s = 0; s < 4; ++s) p.v[s] = stream_load(vp + 16 * s);
     const int64_t si = (int64_t)phys * a.hkv + kh;
     p.ks = a.k_scale[si];
     p.vs = a.v_scale[si];
@@ -212,14 +230,14 @@ __device__ __forceinline__ void load_page(Page<KV_F32>& p, const Args& a, int ph
     const int64_t off = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
     const float* kb = static_cast<const float*>(a.k) + off;
     const float* vb = static_cast<const float*>(a.v) + off;
-    const f32x4* kp = reinterpret_cast<const f32x4*>(kb + l16 * kHeadDim + 4 * g);
+    const f32x4* kp = reinterpret_cast<const f32x4*>(k_fragment(kb, 16 * g + l16));
     const f32x4* vp = reinterpret_cast<const f32x4*>(vb + 4 * g * kHeadDim + 8 * l16);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) p.k[c] = kp[4 * c];
+    for (int c = 0; c < 8; ++c) p.k[c] = stream_load(kp + 64 * c);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        p.v[2 * s] = vp[32 * s];
-        p.v[2 * s + 1] = vp[32 * s + 1];
+        p.v[2 * s] = stream_load(vp + 32 * s);
+        p.v[2 * s + 1] = stream_load(vp + 32 * s + 1);
     }
 }
 

@@ -165,21 +165,17 @@ def one_hot(case, rng):
             uu = float(u[b, kh] @ u[b, kh])
             lam = lam_min / (case.scale * uu)
             pages = case.block_table[b, :W.pages_for(L)]
-            if case.kv_dtype == "bf16":
-                case.k_pool[pages, kh, :, :] = 0
-            elif case.kv_dtype == "fp8":
-                case.k_pool[pages, kh, :, :] = 0
+            case.k_pool[pages, kh] = 0
+            if case.kv_dtype == "fp8":
                 case.k_scale[pages, kh] = 1.0
-            else:
-                case.k_pool[pages, kh, :, :] = 0.0
             p, slot = pages[js[kh] // 16], js[kh] % 16
             row = (lam * u[b, kh]).astype(np.float32)
             if case.kv_dtype == "bf16":
-                case.k_pool[p, kh, slot] = W.bf16_bits(row)
+                W.set_k_token(case.k_pool, p, kh, slot, W.bf16_bits(row))
             elif case.kv_dtype == "fp8":
-                case.k_pool[p, kh, slot] = W.e4m3_bytes(row)
+                W.set_k_token(case.k_pool, p, kh, slot, W.e4m3_bytes(row))
             else:
-                case.k_pool[p, kh, slot] = row
+                W.set_k_token(case.k_pool, p, kh, slot, row)
     return jstar
 
 

@@ -268,7 +268,7 @@ def _scatter(kc, vc, tables, num_pages, fill=np.nan):
         for t in range(kk.shape[0]):
             kp[tab[t // 16], :, t % 16] = kk[t]
             vp[tab[t // 16], :, t % 16] = vv[t]
-    return kp, vp
+    return W.k_to_pool(kp), vp
 
 
 def _table(tabs):
@@ -355,7 +355,8 @@ def test_bf16_pool_reads_same_values_as_f32_pool():
     as_f32 = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
     a = oracle.paged_attention(case.k_pool, case.v_pool, "bf16", case.q, "bf16",
                                case.block_table, case.seq_lens, 1, case.scale)
-    b = oracle.paged_attention(as_f32(case.k_pool), as_f32(case.v_pool), "f32",
+    k32 = W.k_to_pool(as_f32(W.k_from_pool(case.k_pool)))
+    b = oracle.paged_attention(k32, as_f32(case.v_pool), "f32",
                                as_f32(case.q), "f32", case.block_table, case.seq_lens, 1,
                                case.scale)
     assert (a == b).all()
@@ -387,7 +388,7 @@ def test_fp8_identical_pages_give_mean_value():
     tab = [[2, 0, 1]]
     kbyte = W.e4m3_bytes(_rng(24).standard_normal((hkv, d)))
     vbyte = W.e4m3_bytes(_rng(25).standard_normal((3, hkv, 16, d)))
-    kp = np.broadcast_to(kbyte[None, :, None, :], (3, hkv, 16, d)).copy()
+    kp = W.k_to_pool(np.broadcast_to(kbyte[None, :, None, :], (3, hkv, 16, d)).copy())
     vp = vbyte
     ks = np.full((3, hkv), 0.5, dtype=np.float32)
     vs = np.array([[0.25, 2.0], [1.0, 0.5], [4.0, 0.125]], dtype=np.float32)
@@ -398,6 +399,16 @@ def test_fp8_identical_pages_give_mean_value():
     logical = np.concatenate([dec[p] for p in tab[0]], axis=1)          # [hkv][48][d]
     for h in range(hq):
         np.testing.assert_allclose(got[0, 0, h], logical[h // 2].mean(axis=0), atol=1e-13)
+
+
+def test_chunked_k_layout_index_formula():
+    # element d of token t of a slab sits at ((d / x) * 16 + t) * x + d % x
+    for dt, x in ((np.float32, 4), (np.uint16, 8), (np.uint8, 16)):
+        tok = np.arange(16 * 128).reshape(16, 128).astype(dt)
+        pool = W.k_to_pool(tok).reshape(-1)
+        t, d = 5, 77
+        assert pool[((d // x) * 16 + t) * x + d % x] == tok[t, d]
+        assert (W.k_from_pool(W.k_to_pool(tok)) == tok).all()
 
 
 def test_paged_rejects_out_of_range_page():

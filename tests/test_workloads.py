@@ -72,8 +72,9 @@ def test_poison_marks_unused_slots():
                        num_pages=5)
     _check_table(case)
     p_last0 = case.block_table[0, 1]
-    assert (case.k_pool[p_last0, :, 4:] == W.BF16_NAN).all()
-    assert (case.k_pool[p_last0, :, :4] != W.BF16_NAN).all()
+    k_tok = W.k_from_pool(case.k_pool)
+    assert (k_tok[p_last0, :, 4:] == W.BF16_NAN).all()
+    assert (k_tok[p_last0, :, :4] != W.BF16_NAN).all()
     unused = sorted(set(range(5)) - set(case.block_table[case.block_table >= 0].tolist()))
     assert unused and (case.v_pool[unused] == W.BF16_NAN).all()
 
@@ -84,6 +85,6 @@ def test_fp8_scales_are_absmax_over_448():
     # the largest byte of each live slab encodes +-448 (absmax / scale = 448)
     for p in case.block_table[0, :3]:
         live = 16 if p != case.block_table[0, 2] else 8
-        slab = case.k_pool[p, 0, :live]
+        slab = W.k_from_pool(case.k_pool)[p, 0, :live]
         assert (slab & 0x7F).max() == 0x7E
     assert np.isfinite(case.k_scale).all() and (case.k_scale > 0).all()

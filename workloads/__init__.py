@@ -7,7 +7,11 @@ only draws random numbers, rounds them to the storage formats and lays them
 out in the documented pool layout.
 
 Layouts (shared contract, documented in ``include/paged_attn.h``):
-  K pool, V pool  [num_pages][Hkv][page_size=16][D]   (token-major slabs)
+  V pool          [num_pages][Hkv][page_size=16][D]   (token-major slabs)
+  K pool          [num_pages][Hkv][D/x][16][x], x = 16 bytes / element size
+                  (the head dimension cut into 16-byte chunks, each chunk
+                  holding the 16 tokens in turn); ``k_to_pool`` /
+                  ``k_from_pool`` convert from / to token-major slabs
   k_scale/v_scale [num_pages][Hkv] float32           (fp8 pools only)
   Q               [batch][q_per_seq][Hq][D]
   block_table     [batch][max_pages] int32, -1 past a sequence's last page
@@ -75,6 +79,26 @@ def e4m3_bytes(x) -> np.ndarray:
     if nan.any():
         r[nan] = E4M3_NAN
     return r
+
+
+def k_to_pool(k_tokens: np.ndarray) -> np.ndarray:
+    """Token-major K slabs [..., 16, D] -> the pool's chunked K layout [..., D/x, 16, x]."""
+    x = 16 // k_tokens.dtype.itemsize
+    sh = k_tokens.shape
+    a = k_tokens.reshape(sh[:-1] + (sh[-1] // x, x))          # [..., 16, D/x, x]
+    return np.ascontiguousarray(np.swapaxes(a, -3, -2))        # [..., D/x, 16, x]
+
+
+def k_from_pool(k_pool: np.ndarray) -> np.ndarray:
+    """The pool's chunked K layout [..., D/x, 16, x] -> token-major slabs [..., 16, D]."""
+    a = np.swapaxes(k_pool, -3, -2)                             # [..., 16, D/x, x]
+    return np.ascontiguousarray(a).reshape(a.shape[:-2] + (-1,))
+
+
+def set_k_token(k_pool: np.ndarray, page: int, kv_head: int, slot: int, row) -> None:
+    """Write one token's K row (already in the storage dtype) into the chunked pool."""
+    c, _, x = k_pool.shape[-3:]
+    k_pool[page, kv_head, :, slot, :] = np.asarray(row, dtype=k_pool.dtype).reshape(c, x)
 
 
 def pages_for(length: int) -> int:
@@ -173,8 +197,8 @@ class Case:
     seq_lens: np.ndarray    # [B] int32
     block_table: np.ndarray  # [B][max_pages] int32
     num_pages: int
-    k_pool: np.ndarray      # float32 | uint16 (bf16 bits) | uint8 (E4M3)
-    v_pool: np.ndarray
+    k_pool: np.ndarray      # chunked K layout; float32 | uint16 (bf16 bits) | uint8 (E4M3)
+    v_pool: np.ndarray      # token-major V layout, same dtype
     q: np.ndarray           # float32 | uint16
     k_scale: Optional[np.ndarray] = None   # [num_pages][Hkv] float32 (fp8)
     v_scale: Optional[np.ndarray] = None
@@ -290,6 +314,8 @@ def make_case(name: str, *, batch: int, q_per_seq: int, num_q_heads: int,
         k_pool, v_pool = k, v
     else:
         raise ValueError(kv_dtype)
+
+    k_pool = k_to_pool(k_pool)
 
     if q_dtype == "bf16":
         qa = bf16_bits(q)

@@ -56,6 +56,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // never inf - inf; masked scores are -inf and give exp2(-inf) = 0.
 constexpr float kNoMax = -1.0e30f;
 constexpr int kAccStride = kHeadDim + 4;    // LDS row stride of the wave merge (bank skew)
+// The running max of a row moves only when a page's max exceeds it by more
+// than this many log2 units, so weights stay <= 2^8 (safe in fp32 and bf16)
+// and the accumulator is rescaled on few pages.
+constexpr float kRescaleSlack = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -339,49 +343,61 @@ __device__ __forceinline__ f32x4 scores(const Page<KV_F32>& p, const QFrag<KV_F3
 // o[db] holds O[row l16][32g + 8v + db], v = 0..3 (the PV output layout)
 template <int KV> struct Acc { f32x4 o[8]; };
 
-// acc += P * V for one tile; p[s] is the weight of token 4g + s for row l16.
-// Returns the weights as rounded for the product (bf16 paths) so that the
-// running sum uses the same values.
-__device__ __forceinline__ float pv(Acc<KV_BF16>& acc, const Page<KV_BF16>& pg, const float (&p)[4])
+// V of one page as PV A operands: a[db] = {V[4g + s][8 l16 + db], s = 0..3},
+// built once per page and shared by every row tile.
+struct VOps {
+    i16x4 a[8];
+    float vs;       // V scale folded into the probabilities (1 for bf16)
+};
+
+__device__ __forceinline__ void transpose_v(VOps& o, const u32x4 (&v)[4])
 {
-    uint32_t b[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = bf16_bits(p[s]);
-    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
         const int w = db >> 1;
         const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(pg.v[1][w], pg.v[0][w], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(pg.v[3][w], pg.v[2][w], sel);
-        const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
-        acc.o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc.o[db], 0, 0, 0);
+        const uint32_t lo = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+        o.a[db] = __builtin_bit_cast(i16x4, u32x2{lo, hi});
     }
-    return bf16_float(b[0]) + bf16_float(b[1]) + bf16_float(b[2]) + bf16_float(b[3]);
 }
 
-__device__ __forceinline__ float pv(Acc<KV_FP8>& acc, const Page<KV_FP8>& pg, const float (&p)[4])
+__device__ __forceinline__ void prepare_v(VOps& o, const Page<KV_BF16>& pg)
 {
-    uint32_t b[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = bf16_bits(p[s] * pg.vs);
-    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
+    transpose_v(o, pg.v);
+    o.vs = 1.0f;
+}
+
+__device__ __forceinline__ void prepare_v(VOps& o, const Page<KV_FP8>& pg)
+{
     u32x4 vb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) vb[s] = fp8x8_to_bf16x8(pg.v[s][0], pg.v[s][1]);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const int w = db >> 1;
-        const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(vb[1][w], vb[0][w], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(vb[3][w], vb[2][w], sel);
-        const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
-        acc.o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc.o[db], 0, 0, 0);
-    }
-    return p[0] + p[1] + p[2] + p[3];
+    transpose_v(o, vb);
+    o.vs = pg.vs;
 }
 
-__device__ __forceinline__ float pv(Acc<KV_F32>& acc, const Page<KV_F32>& pg, const float (&p)[4])
+// acc += P * V for one tile; p[s] is the weight of token 4g + s for row l16.
+// Returns the sum of the weights as they entered the product (bf16-rounded
+// for bf16 K/V, so the running sum matches the products).
+template <int KV>
+__device__ __forceinline__ float pv(Acc<KV>& acc, const VOps& vo, const float (&p)[4])
+{
+    uint32_t b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = bf16_bits(KV == KV_FP8 ? p[s] * vo.vs : p[s]);
+    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+        acc.o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo.a[db], pb, acc.o[db], 0, 0, 0);
+    if constexpr (KV == KV_FP8)
+        return p[0] + p[1] + p[2] + p[3];
+    else
+        return bf16_float(b[0]) + bf16_float(b[1]) + bf16_float(b[2]) + bf16_float(b[3]);
+}
+
+__device__ __forceinline__ float pv_f32(Acc<KV_F32>& acc, const Page<KV_F32>& pg,
+                                       const float (&p)[4])
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -404,8 +420,20 @@ __device__ __forceinline__ void store_out(float* o, float x) { *o = x; }
 // ---------------------------------------------------------------------------
 // partition kernel
 // ---------------------------------------------------------------------------
+// Occupancy hints measured on MI355X.  Two row tiles (the verify shape) ask
+// for two waves per SIMD: without the hint the compiler spends 272 VGPRs and
+// only one wave per SIMD keeps pages in flight (verify 40 -> 33 us).  The
+// fp8 one-tile kernel with a two-page pipeline fits four waves per SIMD in
+// 116 VGPRs (2% faster).  Larger pipelines keep the compiler's choice, which
+// does not spill.
+template <int KV, int NT, int PF>
+constexpr int min_waves_per_simd()
+{
+    return (NT == 2 && KV != KV_F32) ? 2 : (NT == 1 && KV == KV_FP8 && PF == 2) ? 4 : 1;
+}
+
 template <int KV, int NT, int W, int PF>
-__global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
+__global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void paged_attn_partition(Args a)
 {
     constexpr int RT = 16 * NT;   // rows per workgroup
     __shared__ float sm_ml[W][RT][2];
@@ -473,6 +501,7 @@ __global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
     auto consume = [&](Page<KV>& pg, int j) {
         const int base = (pg0 + wave + j * W) * kPage;
         const bool need_mask = base + kPage - 1 > first_limit;
+        VOps vo;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 sv = scores(pg, qf[nt]);
@@ -485,16 +514,25 @@ __global__ __launch_bounds__(W * kWave) void paged_attn_partition(Args a)
                     s[v] = (base + 4 * g + v <= lim[nt]) ? s[v] : -INFINITY;
             }
             const float mx = group_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-            const float mnew = fmaxf(m[nt], mx);
-            const float alpha = fast_exp2(m[nt] - mnew);
-            m[nt] = mnew;
+            const bool grow = mx > m[nt] + kRescaleSlack;
+            if (__any(grow)) {
+                const float mnew = grow ? mx : m[nt];
+                const float alpha = fast_exp2(m[nt] - mnew);
+                m[nt] = mnew;
+                l[nt] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) acc[nt].o[db] *= alpha;
+            }
             float p[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mnew);
-#pragma unroll
-            for (int db = 0; db < 8; ++db) acc[nt].o[db] *= alpha;
+            for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - m[nt]);
             if (nt == 0 && base + kPage > L) clear_dead_v(pg, L - base - 4 * g);
-            l[nt] = l[nt] * alpha + pv(acc[nt], pg, p);
+            if constexpr (KV == KV_F32) {
+                l[nt] += pv_f32(acc[nt], pg, p);
+            } else {
+                if (nt == 0) prepare_v(vo, pg);
+                l[nt] += pv<KV>(acc[nt], vo, p);
+            }
         }
     };
 
@@ -748,10 +786,10 @@ void launch_partition(const Args& a, int grid, hipStream_t st)
 template <int KV, int NT>
 void launch_tuned(int waves, int prefetch, const Args& a, int grid, hipStream_t st)
 {
-    if (KV == KV_F32 || NT > 2) {
+    if constexpr (KV == KV_F32 || NT > 2) {
         launch_partition<KV, NT, kWaves, 2>(a, grid, st);
         return;
-    }
+    } else {
     const int key = waves * 10 + prefetch;
     switch (key) {
     case 42: launch_partition<KV, NT, 4, 2>(a, grid, st); break;
@@ -761,6 +799,7 @@ void launch_tuned(int waves, int prefetch, const Args& a, int grid, hipStream_t 
     case 84: launch_partition<KV, NT, 8, 4>(a, grid, st); break;
     case 82: launch_partition<KV, NT, 8, 2>(a, grid, st); break;
     default: launch_partition<KV, NT, 4, 2>(a, grid, st); break;
+    }
     }
 }
 

@@ -25,8 +25,9 @@
 //    scores, v_exp_f32), running max reduced across the 4 lane groups with
 //    two shuffles per page; the running sum stays lane-local until the end.
 //  * Waves of a workgroup are merged in LDS in a fixed order; context
-//    partitions (split-K) are merged by a second small kernel.  Both merges
-//    use the same rescaling: weight 2^(m_part - m_max).
+//    partitions (split-K, at most 64 per sequence) are merged by a second
+//    small kernel, one workgroup per output row.  Both merges weight a part
+//    by 2^(m_part - m_max).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -51,6 +52,7 @@ constexpr int kHeadDim = 128;
 constexpr int kSlab = kPage * kHeadDim;     // elements of one (page, kv head) slab
 constexpr int kWave = 64;
 constexpr int kMaxRowTiles = 4;             // 16-row MFMA tiles per workgroup
+constexpr int kMaxSplits = 64;              // context partitions per sequence
 constexpr float kLog2e = 1.4426950408889634f;
 // Running max before any key is seen.  Finite, so exp2(m_old - m_new) is
 // never inf - inf; masked scores are -inf and give exp2(-inf) = 0.
@@ -630,32 +632,52 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
 }
 
 // ---------------------------------------------------------------------------
-// split-K reduce: one wave per (sequence, query row, head), two dims per lane
+// split-K reduce: one 128-thread workgroup per output row (sequence, query
+// row, head), one head-dim element per thread.  The first 16 partials of the
+// element are fetched in the same round as the row's (max, sum) pairs, so a
+// merge of up to 16 partitions costs one memory round trip.
 // ---------------------------------------------------------------------------
+constexpr int kReduceThreads = kHeadDim;
+constexpr int kReduceInFlight = 16;
+
 template <typename OT>
-__global__ __launch_bounds__(kWave) void paged_attn_reduce(Args a)
+__global__ __launch_bounds__(kReduceThreads) void paged_attn_reduce(Args a)
 {
+    __shared__ float sm_m[kMaxSplits];
+    __shared__ float sm_l[kMaxSplits];
     const int64_t orow = blockIdx.x;                 // (b * n + i) * hq + h
     const int b = (int)(orow / ((int64_t)a.n * a.hq));
     const int L = min(a.seq_lens[b], a.max_pages * kPage);
     const int npages = (L + kPage - 1) / kPage;
     const int ns = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
     if (ns <= 1) return;                             // written by the partition kernel
-    const float* ml = a.part_ml + orow * a.num_splits * 2;
-    float mm = kNoMax;
-    for (int s = 0; s < ns; ++s) mm = fmaxf(mm, ml[2 * s]);
-    const int d = 2 * threadIdx.x;
-    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    const float* pa = a.part_acc + orow * a.num_splits * kHeadDim + d;
-    for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(ml[2 * s] - mm);
-        lsum += ml[2 * s + 1] * w;
-        o0 += pa[s * kHeadDim] * w;
-        o1 += pa[s * kHeadDim + 1] * w;
+    const int t = threadIdx.x;
+    const float* src = a.part_acc + orow * a.num_splits * kHeadDim + t;
+    float x[kReduceInFlight];
+#pragma unroll
+    for (int sp = 0; sp < kReduceInFlight; ++sp) x[sp] = sp < ns ? src[sp * kHeadDim] : 0.f;
+    if (t < ns) {
+        const float* ml = a.part_ml + (orow * a.num_splits + t) * 2;
+        sm_m[t] = ml[0];
+        sm_l[t] = ml[1];
     }
-    OT* out = static_cast<OT*>(a.out) + orow * kHeadDim + d;
-    store_out(out, o0 / lsum);
-    store_out(out + 1, o1 / lsum);
+    __syncthreads();
+    float mm = kNoMax;
+    for (int sp = 0; sp < ns; ++sp) mm = fmaxf(mm, sm_m[sp]);
+    float ls = 0.f, acc = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kReduceInFlight; ++sp)
+        if (sp < ns) {
+            const float w = fast_exp2(sm_m[sp] - mm);
+            ls += sm_l[sp] * w;
+            acc += w * x[sp];
+        }
+    for (int sp = kReduceInFlight; sp < ns; ++sp) {
+        const float w = fast_exp2(sm_m[sp] - mm);
+        ls += sm_l[sp] * w;
+        acc += w * src[sp * kHeadDim];
+    }
+    store_out(static_cast<OT*>(a.out) + orow * kHeadDim + t, acc / ls);
 }
 
 // ---------------------------------------------------------------------------
@@ -743,7 +765,9 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     if (d.partition_pages > 0) {
         part = std::min(d.partition_pages, max_pages);
     } else {
-        const int64_t target = 2LL * cu_count();
+        // two workgroups per CU for one row tile; one for wider query tiles,
+        // whose workgroups already fill the register file (MI355X sweep)
+        const int64_t target = (nt == 1 ? 2LL : 1LL) * cu_count();
         int64_t ns = (target + units - 1) / units;
         const int64_t ns_cap =
             std::max<int64_t>(1, max_pages / (2 * (d.waves > 0 ? d.waves : kWaves)));
@@ -752,6 +776,7 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     }
     const int waves = d.waves > 0 ? d.waves : kWaves;
     part = std::min(part, 64 * waves);         // each wave holds at most 64 page ids
+    part = std::max(part, (max_pages + kMaxSplits - 1) / kMaxSplits);
     const int64_t ns = (max_pages + part - 1) / part;
     const int64_t grid = units * ns;
     if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
@@ -894,12 +919,12 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), st)) != hipSuccess)
         return hip_fail(e, "hipEventRecord(end)");
     if (pl.reduce) {
-        const int64_t rows_out = (int64_t)batch * n * hq;
+        const unsigned rows_out = (unsigned)((int64_t)batch * n * hq);
         if (q_dtype == PA_F32)
-            hipLaunchKernelGGL(paged_attn_reduce<float>, dim3((unsigned)rows_out), dim3(kWave), 0,
+            hipLaunchKernelGGL(paged_attn_reduce<float>, dim3(rows_out), dim3(kReduceThreads), 0,
                                st, a);
         else
-            hipLaunchKernelGGL(paged_attn_reduce<uint16_t>, dim3((unsigned)rows_out), dim3(kWave),
+            hipLaunchKernelGGL(paged_attn_reduce<uint16_t>, dim3(rows_out), dim3(kReduceThreads),
                                0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "reduce kernel launch");
     }

@@ -89,6 +89,13 @@ def test_plans_for_named_workloads():
     LIB.paged_attn_destroy_pool(h)
 
 
+def test_split_count_is_capped():
+    st, h = _create(num_pages=8192, partition_pages=1)
+    pl = _plan(h, 1, 1, 8, 32768)                    # 2048 pages, asked 1 page each
+    assert pl.num_splits <= 64 and pl.num_splits * pl.partition_pages >= 2048
+    LIB.paged_attn_destroy_pool(h)
+
+
 def test_workspace_sizes():
     st, h = _create(num_pages=8192)
     n = ctypes.c_size_t()

@@ -258,6 +258,40 @@ def test_split_sizes_agree(pa):
         check(run_gpu(pa, case, part, dev=dev), ref, "f32", f"part={part} vs auto")
 
 
+def test_workspace_reuse_and_partition_merge(pa):
+    """The in-kernel split merge leaves its counters at zero: one workspace
+    serves repeated calls and a differently shaped call, bit for bit."""
+    big = small_case("bf16", 5, 32, 8, [4101, 700, 90], seed=61)
+    d = to_device(big)
+    pool = pa.paged_attn_create_pool(d.k, d.v, None, None, 7)
+    plan = pa.paged_attn_plan(pool, big.batch, 5, 32, big.max_seq_len)
+    assert plan["reduce"] == 1 and plan["num_splits"] > 1
+    ws = pa.workspace_for(pool, d.q, big.max_seq_len)
+    outs = []
+    for _ in range(3):
+        o = torch.empty_like(d.q)
+        pa.paged_attn_verify(pool, d.q, o, d.block_table, d.seq_lens, big.max_seq_len,
+                             big.scale, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    check(to_numpy_f64(outs[0]), run_oracle(big), "bf16", "reused workspace")
+    small = small_case("bf16", 1, 32, 8, [1000, 33], seed=62)
+    ds = to_device(small)
+    pool2 = pa.paged_attn_create_pool(ds.k, ds.v, None, None, 3)
+    assert pa.paged_attn_workspace_bytes(pool2, 2, 1, 32, small.max_seq_len) <= ws.numel()
+    o2 = torch.empty_like(ds.q)
+    pa.paged_attn_verify(pool2, ds.q, o2, ds.block_table, ds.seq_lens, small.max_seq_len,
+                         small.scale, ws)
+    torch.cuda.synchronize()
+    check(to_numpy_f64(o2), run_oracle(small), "bf16", "second shape, same workspace")
+
+
+def test_sixty_four_partitions(pa):
+    case = small_case("f32", 1, 8, 2, [16 * 64 * 3, 100], seed=63)
+    check(run_gpu(pa, case, 1), run_oracle(case), "f32", "64 partitions of 3 pages")
+
+
 def test_decode_entry_point_matches_verify(pa):
     case = small_case("bf16", 1, 32, 8, [300, 2048, 17], seed=97)
     d = to_device(case)

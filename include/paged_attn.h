@@ -94,7 +94,8 @@ typedef struct pa_pool_desc {
     const float* v_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
     int32_t partition_pages;  /* split-K partition length in pages; 0 = chosen per call */
     int32_t waves;            /* tuning: waves per workgroup (4 or 8); 0 = automatic */
-    int32_t prefetch;         /* tuning: pages held in registers per wave (2..4); 0 = automatic */
+    int32_t prefetch;         /* tuning: pages held in registers per wave (2..6, at most 4 with
+                                 8 waves); 0 = automatic */
 } pa_pool_desc;
 
 typedef struct pa_pool pa_pool;

@@ -282,13 +282,14 @@ template <> struct QFrag<KV_BF16> { bf16x8 b[4]; };   // dims 32c + 8g .. +8
 template <> struct QFrag<KV_FP8>  { bf16x8 b[4]; };   // dims 64(c/2) + 16g + 8(c%2) .. +8
 template <> struct QFrag<KV_F32>  { f32x4 b[8]; };    // dims 16c + 4g .. +4
 
+// Loads are unconditional (the row pointer of a padding row is a valid row)
+// and padding rows are zeroed afterwards, so the loads can stay in flight.
 __device__ __forceinline__ void load_q(QFrag<KV_BF16>& f, const uint16_t* row, bool valid, int g)
 {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        u32x4 x = valid ? *reinterpret_cast<const u32x4*>(row + 32 * c + 8 * g)
-                        : u32x4{0u, 0u, 0u, 0u};
-        f.b[c] = __builtin_bit_cast(bf16x8, x);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(row + 32 * c + 8 * g);
+        f.b[c] = __builtin_bit_cast(bf16x8, valid ? x : u32x4{0u, 0u, 0u, 0u});
     }
 }
 __device__ __forceinline__ void load_q(QFrag<KV_FP8>& f, const uint16_t* row, bool valid, int g)
@@ -296,16 +297,17 @@ __device__ __forceinline__ void load_q(QFrag<KV_FP8>& f, const uint16_t* row, bo
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int d0 = 64 * (c >> 1) + 16 * g + 8 * (c & 1);
-        u32x4 x = valid ? *reinterpret_cast<const u32x4*>(row + d0) : u32x4{0u, 0u, 0u, 0u};
-        f.b[c] = __builtin_bit_cast(bf16x8, x);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(row + d0);
+        f.b[c] = __builtin_bit_cast(bf16x8, valid ? x : u32x4{0u, 0u, 0u, 0u});
     }
 }
 __device__ __forceinline__ void load_q(QFrag<KV_F32>& f, const float* row, bool valid, int g)
 {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        f.b[c] = valid ? *reinterpret_cast<const f32x4*>(row + 16 * c + 4 * g)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 8; ++c) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(row + 16 * c + 4 * g);
+        f.b[c] = valid ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 }
 
 // S^T[token][row] for one 16-row tile: lane holds tokens 4g + v of row l16
@@ -426,12 +428,12 @@ __device__ __forceinline__ void store_out(float* o, float x) { *o = x; }
 // for two waves per SIMD: without the hint the compiler spends 272 VGPRs and
 // only one wave per SIMD keeps pages in flight (verify 40 -> 33 us).  The
 // fp8 one-tile kernel with a two-page pipeline fits four waves per SIMD in
-// 116 VGPRs (2% faster).  Larger pipelines keep the compiler's choice, which
-// does not spill.
+// 116 VGPRs (2% faster).  Deeper pipelines keep the compiler's choice, which
+// does not spill; they are meant for plans with one workgroup per CU.
 template <int KV, int NT, int PF>
 constexpr int min_waves_per_simd()
 {
-    return (NT == 2 && KV != KV_F32) ? 2 : (NT == 1 && KV == KV_FP8 && PF == 2) ? 4 : 1;
+    return (NT == 2 && KV != KV_F32 && PF <= 3) ? 2 : (NT == 1 && KV == KV_FP8 && PF == 2) ? 4 : 1;
 }
 
 template <int KV, int NT, int W, int PF>
@@ -455,22 +457,17 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     const int kh = unit % a.hkv;
     const int b = unit / a.hkv;
 
-    // lengths are clamped to what the block table can describe, and page ids
-    // to the pool, so that arrays breaking the contract give wrong numbers
-    // but never an access outside the caller's buffers
-    const int L = min(a.seq_lens[b], a.max_pages * kPage);
-    const int npages = (L + kPage - 1) / kPage;
-    const int nsplit_b = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
-    if (split >= nsplit_b) return;
+    // Block-table ids and query rows do not depend on the sequence length,
+    // so they are requested together with it: the first page loads then wait
+    // for one memory round trip instead of two.
     const int pg0 = split * a.part_pages;
-    const int pg1 = min(pg0 + a.part_pages, npages);
     const int row0 = rc * RT;
-    const int rows_here = min(RT, a.rows - row0);
-    const int first_limit = L - a.n;          // row 0 sees tokens 0 .. L - n
-
-    // query fragments and per-row visibility limits
+    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+    // (unconditional loads from clamped, in-bounds addresses: a lane-masked
+    // load would make the compiler wait for it on the spot)
+    const int raw_id = bt_row[min(pg0 + wave + lane * W, min(pg0 + a.part_pages, a.max_pages) - 1)];
     QFrag<KV> qf[NT];
-    int lim[NT];
+    int qi[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int r = row0 + nt * 16 + l16;
@@ -481,8 +478,24 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
             static_cast<const typename QPtr<KV>::type*>(a.q) +
             (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim;
         load_q(qf[nt], qrow, valid, g);
-        lim[nt] = valid ? first_limit + i : L - 1;
+        qi[nt] = valid ? i : -1;
     }
+
+    // lengths are clamped to what the block table can describe, and page ids
+    // to the pool, so that arrays breaking the contract give wrong numbers
+    // but never an access outside the caller's buffers
+    const int L = min(a.seq_lens[b], a.max_pages * kPage);
+    const int npages = (L + kPage - 1) / kPage;
+    const int nsplit_b = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
+    if (split >= nsplit_b) return;
+    const int pg1 = min(pg0 + a.part_pages, npages);
+    const int rows_here = min(RT, a.rows - row0);
+    const int first_limit = L - a.n;          // row 0 sees tokens 0 .. L - n
+
+    // per-row visibility limits (padding rows see every live token)
+    int lim[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lim[nt] = qi[nt] >= 0 ? first_limit + qi[nt] : L - 1;
 
     Acc<KV> acc[NT];
     float m[NT], l[NT];
@@ -496,9 +509,7 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
 
     // this wave's pages: pg0 + wave + j * W, j < nj (nj <= 64 by construction)
     const int nj = (pg1 - pg0 - wave + W - 1) / W;
-    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-    const int my_id = (lane < nj) ? min(max(bt_row[pg0 + wave + lane * W], 0), a.num_pages - 1)
-                                  : 0;
+    const int my_id = (lane < nj) ? min(max(raw_id, 0), a.num_pages - 1) : 0;
 
     auto consume = [&](Page<KV>& pg, int j) {
         const int base = (pg0 + wave + j * W) * kPage;
@@ -820,6 +831,8 @@ void launch_tuned(int waves, int prefetch, const Args& a, int grid, hipStream_t 
     case 42: launch_partition<KV, NT, 4, 2>(a, grid, st); break;
     case 43: launch_partition<KV, NT, 4, 3>(a, grid, st); break;
     case 44: launch_partition<KV, NT, 4, 4>(a, grid, st); break;
+    case 45: launch_partition<KV, NT, 4, 5>(a, grid, st); break;
+    case 46: launch_partition<KV, NT, 4, 6>(a, grid, st); break;
     case 83: launch_partition<KV, NT, 8, 3>(a, grid, st); break;
     case 84: launch_partition<KV, NT, 8, 4>(a, grid, st); break;
     case 82: launch_partition<KV, NT, 8, 2>(a, grid, st); break;
@@ -966,8 +979,9 @@ PA_API pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out)
     if (desc->partition_pages < 0) return fail(PA_ERR_INVALID_ARG, "partition_pages must be >= 0");
     if (desc->waves != 0 && desc->waves != 4 && desc->waves != 8)
         return fail(PA_ERR_UNSUPPORTED, "waves must be 0, 4 or 8");
-    if (desc->prefetch != 0 && (desc->prefetch < 2 || desc->prefetch > 4))
-        return fail(PA_ERR_UNSUPPORTED, "prefetch must be 0 or 2..4");
+    if (desc->prefetch != 0 && (desc->prefetch < 2 || desc->prefetch > 6 ||
+                                (desc->waves == 8 && desc->prefetch > 4)))
+        return fail(PA_ERR_UNSUPPORTED, "prefetch must be 0, 2..6 (2..4 with 8 waves)");
     pa_pool* p = new (std::nothrow) pa_pool;
     if (!p) return fail(PA_ERR_INVALID_ARG, "out of host memory");
     p->d = *desc;

@@ -56,6 +56,7 @@ def _create(**kw):
     (dict(partition_pages=-1), B.PA_ERR_INVALID_ARG),
     (dict(waves=6), B.PA_ERR_UNSUPPORTED),
     (dict(prefetch=9), B.PA_ERR_UNSUPPORTED),
+    (dict(waves=8, prefetch=5), B.PA_ERR_UNSUPPORTED),
 ])
 def test_create_pool_rejects(kw, status):
     st, h = _create(**kw)

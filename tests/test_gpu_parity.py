@@ -114,7 +114,9 @@ def test_tuning_variants(pa, kv, n):
     ref = run_oracle(case)
     dev = to_device(case)
     for waves in (4, 8):
-        for prefetch in (2, 3, 4):
+        for prefetch in (2, 3, 4, 5, 6):
+            if waves == 8 and prefetch > 4:
+                continue
             for part in (0, 7):
                 check(run_gpu(pa, case, part, dev=dev, waves=waves, prefetch=prefetch), ref, kv,
                       f"waves={waves} prefetch={prefetch} part={part}")

@@ -76,7 +76,8 @@ def cpu_baseline(case, reps):
     def one(b):
         oracle.paged_attention(case.k_pool, case.v_pool, case.kv_dtype, case.q, case.q_dtype,
                                case.block_table, case.seq_lens, case.q_per_seq, case.scale,
-                               seqs=[b], k_scale=case.k_scale, v_scale=case.v_scale)
+                               seqs=[b], k_scale=case.k_scale, v_scale=case.v_scale,
+                               tree_mask=case.tree_mask)
 
     times = []
     with cf.ThreadPoolExecutor(max_workers=cores) as ex:
@@ -139,7 +140,8 @@ def main():
 
     def call(ev_begin=None, ev_end=None):
         pa.paged_attn_verify(pool, dev.q, out, dev.block_table, dev.seq_lens, case.max_seq_len,
-                             case.scale, ws, ev_begin=ev_begin, ev_end=ev_end)
+                             case.scale, ws, ev_begin=ev_begin, ev_end=ev_end,
+                             tree_mask=dev.tree_mask)
 
     def flush_caches():
         if flush is not None:

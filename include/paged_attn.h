@@ -153,16 +153,35 @@ pa_status paged_attn_verify(const pa_pool* pool, const void* q, pa_dtype q_dtype
                             int32_t num_q_heads, float scale, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* paged_attn_verify that also records ev_begin right before the attention
- * (partition) kernel and ev_end right after it on the same stream, so a
- * caller can time that kernel alone.  The events are hipEvent_t handles
- * created by the caller; either may be NULL. */
+/* Tree verification (Medusa / EAGLE style draft trees; "Batching, speculative
+ * decoding, paged attention" §5.3.13: a tree of candidate branches is verified
+ * in one forward with tree attention).  The q_per_seq <= 64 query rows are the
+ * tree's nodes in topological order, stored as the last q_per_seq tokens of
+ * each sequence (row i is token L - q_per_seq + i, node 0 the root).  Row i
+ * attends to every context token t < L - q_per_seq and to tree token j iff bit
+ * j of tree_mask[b][i] is set: its ancestors and itself.  tree_mask is a device
+ * array [batch][q_per_seq] of uint64; bits >= q_per_seq are ignored.  The chain
+ * mask tree_mask[b][i] = 2^(i+1) - 1 gives exactly paged_attn_verify.  Every
+ * row must see at least one key.  PA_ERR_INVALID_ARG for a null mask,
+ * PA_ERR_UNSUPPORTED for q_per_seq > 64; otherwise as paged_attn_verify. */
+pa_status paged_attn_verify_tree(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                                 void* out, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                 int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                 int32_t num_q_heads, float scale, const uint64_t* tree_mask,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_verify (tree_mask NULL) or paged_attn_verify_tree (tree_mask set)
+ * that also records ev_begin right before the attention (partition) kernel and
+ * ev_end right after it on the same stream, so a caller can time that kernel
+ * alone.  The events are hipEvent_t handles created by the caller; either may
+ * be NULL. */
 pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q_dtype,
                                   void* out, const int32_t* block_table,
                                   int32_t max_pages_per_seq, const int32_t* seq_lens,
                                   int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
-                                  int32_t num_q_heads, float scale, void* workspace,
-                                  size_t workspace_bytes, void* stream,
+                                  int32_t num_q_heads, float scale, const uint64_t* tree_mask,
+                                  void* workspace, size_t workspace_bytes, void* stream,
                                   void* ev_begin, void* ev_end);
 
 /* Debug check of the device-array contract: copies block_table and seq_lens

@@ -50,6 +50,11 @@ def _load():
         i = ctypes.c_int
         lib.oracle_attention.restype = i
         lib.oracle_attention.argtypes = [vp, vp, vp, i, i, i, i, i, ctypes.c_double, vp]
+        lib.oracle_attention_tree.restype = i
+        lib.oracle_attention_tree.argtypes = [vp, vp, vp, i, i, i, i, i, ctypes.c_double, vp, vp]
+        lib.oracle_paged_attention_tree.restype = i
+        lib.oracle_paged_attention_tree.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, i, vp, i,
+                                                    vp, i, i, i, ctypes.c_double, vp, vp, i, vp]
         lib.oracle_paged_attention.restype = i
         lib.oracle_paged_attention.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, i, vp, i,
                                                vp, i, i, i, ctypes.c_double, vp, i, vp]
@@ -90,9 +95,29 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.n
     return out
 
 
+def attention_tree(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   tree_mask) -> np.ndarray:
+    """Tree verification for one sequence: row i sees every context key and
+    the tree keys whose bit is set in tree_mask[i] (uint64, n <= 64)."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    mask = np.ascontiguousarray(tree_mask, dtype=np.uint64)
+    n, hq, d = q.shape
+    length, hkv, d2 = k.shape
+    if v.shape != k.shape or d2 != d or mask.shape != (n,):
+        raise ValueError("shape mismatch")
+    out = np.empty((n, hq, d), dtype=np.float64)
+    rc = _load().oracle_attention_tree(_ptr(q), _ptr(k), _ptr(v), length, n, hq, hkv, d,
+                                       float(scale), _ptr(mask), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_tree rejected its arguments (code {rc})")
+    return out
+
+
 def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
                     seq_lens, q_per_seq: int, scale: float, seqs=None,
-                    k_scale=None, v_scale=None) -> np.ndarray:
+                    k_scale=None, v_scale=None, tree_mask=None) -> np.ndarray:
     """Paged attention read straight from the pool, for the listed sequences.
 
     v_pool: [num_pages][Hkv][page_size][D] as float32 (``f32``), uint16 bf16
@@ -100,7 +125,8 @@ def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
     the chunked K layout [num_pages][Hkv][D/x][page_size][x], x = 16 bytes /
     element size.
     q: [batch][n][Hq][D] float32 or uint16 bf16 bits.  Returns
-    [len(seqs)][n][Hq][D] float64.
+    [len(seqs)][n][Hq][D] float64.  tree_mask: optional [batch][n] uint64
+    ancestor masks (draft-tree verification); None = the causal chain.
     """
     k_pool = np.ascontiguousarray(k_pool)
     v_pool = np.ascontiguousarray(v_pool)
@@ -122,11 +148,16 @@ def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
     if kv_dtype == "fp8":
         ks = np.ascontiguousarray(k_scale, dtype=np.float32)
         vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    mask = None
+    if tree_mask is not None:
+        mask = np.ascontiguousarray(tree_mask, dtype=np.uint64)
+        if mask.shape != (batch, n):
+            raise ValueError("tree_mask must be [batch][q_per_seq]")
     out = np.empty((len(seqs), n, hq, d), dtype=np.float64)
-    rc = _load().oracle_paged_attention(
+    rc = _load().oracle_paged_attention_tree(
         _ptr(k_pool), _ptr(v_pool), _CODES[kv_dtype], _ptr(ks), _ptr(vs),
         num_pages, hkv, page_size, d, _ptr(q), _CODES[q_dtype], _ptr(bt), bt.shape[1],
-        _ptr(lens), batch, n, hq, float(scale), _ptr(seqs), len(seqs), _ptr(out))
+        _ptr(lens), batch, n, hq, float(scale), _ptr(mask), _ptr(seqs), len(seqs), _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_paged_attention rejected its arguments (code {rc})")
     return out

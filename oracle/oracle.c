@@ -41,25 +41,51 @@ double oracle_e4m3_value(uint8_t byte)
     return sign ? -mag : mag;
 }
 
-int oracle_attention(const double* q, const double* k, const double* v,
-                     int L, int n, int Hq, int Hkv, int D, double scale,
-                     double* out)
+/* is key t visible to row i?  (mask == NULL: the causal chain) */
+static int visible(int t, int i, int L, int n, const uint64_t* tree_mask)
+{
+    const int first_new = L - n;            /* the n query rows are the last n tokens */
+    if (t < first_new)
+        return 1;
+    if (!tree_mask)
+        return t <= first_new + i;
+    return (int)((tree_mask[i] >> (t - first_new)) & 1u);
+}
+
+static int attention_rows(const double* q, const double* k, const double* v,
+                          int L, int n, int Hq, int Hkv, int D, double scale,
+                          const uint64_t* tree_mask, double* out)
 {
     if (n < 1 || L < n || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || D < 1)
         return ORACLE_BAD_ARG;
+    if (tree_mask && n > 64)
+        return ORACLE_BAD_ARG;
     const int G = Hq / Hkv;
     double* z = (double*)malloc(sizeof(double) * (size_t)L);
-    if (!z)
+    int* vis = (int*)malloc(sizeof(int) * (size_t)L);
+    if (!z || !vis) {
+        free(z); free(vis);
         return ORACLE_NO_MEMORY;
+    }
 
-    for (int i = 0; i < n; ++i) {
-        /* row i is token L - n + i and sees itself and every earlier key */
-        const int visible = L - n + i + 1;
+    int rc = ORACLE_OK;
+    for (int i = 0; i < n && rc == ORACLE_OK; ++i) {
+        int count = 0;
+        for (int t = 0; t < L; ++t) {
+            vis[t] = visible(t, i, L, n, tree_mask);
+            count += vis[t];
+        }
+        if (count == 0) {
+            rc = ORACLE_BAD_ARG;
+            break;
+        }
         for (int h = 0; h < Hq; ++h) {
             const int hk = h / G;
             const double* qr = q + ((size_t)i * Hq + h) * D;
             double zmax = -INFINITY;
-            for (int t = 0; t < visible; ++t) {
+            for (int t = 0; t < L; ++t) {
+                if (!vis[t])
+                    continue;
                 const double* kt = k + ((size_t)t * Hkv + hk) * D;
                 double dot = 0.0;
                 for (int d = 0; d < D; ++d)
@@ -69,21 +95,42 @@ int oracle_attention(const double* q, const double* k, const double* v,
                     zmax = z[t];
             }
             double denom = 0.0;
-            for (int t = 0; t < visible; ++t) {
+            for (int t = 0; t < L; ++t) {
+                if (!vis[t])
+                    continue;
                 z[t] = exp(z[t] - zmax);
                 denom += z[t];
             }
             double* o = out + ((size_t)i * Hq + h) * D;
             for (int d = 0; d < D; ++d) {
                 double acc = 0.0;
-                for (int t = 0; t < visible; ++t)
-                    acc += z[t] * v[((size_t)t * Hkv + hk) * D + d];
+                for (int t = 0; t < L; ++t)
+                    if (vis[t])
+                        acc += z[t] * v[((size_t)t * Hkv + hk) * D + d];
                 o[d] = acc / denom;
             }
         }
     }
     free(z);
-    return ORACLE_OK;
+    free(vis);
+    return rc;
+}
+
+int oracle_attention(const double* q, const double* k, const double* v,
+                     int L, int n, int Hq, int Hkv, int D, double scale,
+                     double* out)
+{
+    /* row i is token L - n + i and sees itself and every earlier key */
+    return attention_rows(q, k, v, L, n, Hq, Hkv, D, scale, NULL, out);
+}
+
+int oracle_attention_tree(const double* q, const double* k, const double* v,
+                          int L, int n, int Hq, int Hkv, int D, double scale,
+                          const uint64_t* tree_mask, double* out)
+{
+    if (!tree_mask)
+        return ORACLE_BAD_ARG;
+    return attention_rows(q, k, v, L, n, Hq, Hkv, D, scale, tree_mask, out);
 }
 
 /* bytes of one element of the given code */
@@ -107,14 +154,14 @@ static double element(const void* base, int code, size_t idx)
     }
 }
 
-int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
-                           const float* k_scale, const float* v_scale,
-                           int num_pages, int Hkv, int page_size, int D,
-                           const void* q, int q_dtype,
-                           const int32_t* block_table, int max_pages,
-                           const int32_t* seq_lens, int batch, int n, int Hq,
-                           double scale, const int32_t* seqs, int nseqs,
-                           double* out)
+int oracle_paged_attention_tree(const void* k_pool, const void* v_pool, int kv_dtype,
+                                const float* k_scale, const float* v_scale,
+                                int num_pages, int Hkv, int page_size, int D,
+                                const void* q, int q_dtype,
+                                const int32_t* block_table, int max_pages,
+                                const int32_t* seq_lens, int batch, int n, int Hq,
+                                double scale, const uint64_t* tree_mask,
+                                const int32_t* seqs, int nseqs, double* out)
 {
     if (!k_pool || !v_pool || !q || !block_table || !seq_lens || !out || !seqs)
         return ORACLE_BAD_ARG;
@@ -177,11 +224,26 @@ int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
             qc[e] = element(q, q_dtype, (size_t)b * n * Hq * D + e);
 
         int rc = bad ? ORACLE_BAD_TABLE
-                     : oracle_attention(qc, kc, vc, L, n, Hq, Hkv, D, scale,
-                                        out + (size_t)s * n * Hq * D);
+                     : attention_rows(qc, kc, vc, L, n, Hq, Hkv, D, scale,
+                                      tree_mask ? tree_mask + (size_t)b * n : NULL,
+                                      out + (size_t)s * n * Hq * D);
         free(kc); free(vc); free(qc);
         if (rc != ORACLE_OK)
             return rc;
     }
     return ORACLE_OK;
+}
+
+int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
+                           const float* k_scale, const float* v_scale,
+                           int num_pages, int Hkv, int page_size, int D,
+                           const void* q, int q_dtype,
+                           const int32_t* block_table, int max_pages,
+                           const int32_t* seq_lens, int batch, int n, int Hq,
+                           double scale, const int32_t* seqs, int nseqs,
+                           double* out)
+{
+    return oracle_paged_attention_tree(k_pool, v_pool, kv_dtype, k_scale, v_scale, num_pages,
+                                       Hkv, page_size, D, q, q_dtype, block_table, max_pages,
+                                       seq_lens, batch, n, Hq, scale, NULL, seqs, nseqs, out);
 }

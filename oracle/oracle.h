@@ -65,6 +65,20 @@ int oracle_attention(const double* q, const double* k, const double* v,
                      double* out);
 
 /*
+ * Tree verification: the n query rows are the nodes of a draft tree stored in
+ * the last n slots of the sequence (row i is token L - n + i).  Row i sees
+ * every context token t < L - n and tree token j (token L - n + j) iff bit j
+ * of tree_mask[i] is set (its ancestors and itself).  Source: "Batching,
+ * speculative decoding, paged attention" §5.3.13 (Medusa and its relatives
+ * verify a tree of candidate branches in one forward with tree attention).
+ * The chain tree tree_mask[i] = 2^(i+1) - 1 is the causal verify above.
+ * Returns ORACLE_BAD_ARG if n > 64 or a row sees no key at all.
+ */
+int oracle_attention_tree(const double* q, const double* k, const double* v,
+                          int L, int n, int Hq, int Hkv, int D, double scale,
+                          const uint64_t* tree_mask, double* out);
+
+/*
  * Paged attention for the listed sequences, read straight from the pool.
  *   v_pool          [num_pages][Hkv][page_size][D] elements of kv_dtype
  *                   (float32, bfloat16 bits, or E4M3 bytes), token-major
@@ -91,6 +105,17 @@ int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
                            const int32_t* seq_lens, int batch, int n, int Hq,
                            double scale, const int32_t* seqs, int nseqs,
                            double* out);
+
+/* As oracle_paged_attention, with a draft tree per sequence:
+ * tree_mask [batch][n] (NULL = the causal chain). */
+int oracle_paged_attention_tree(const void* k_pool, const void* v_pool, int kv_dtype,
+                                const float* k_scale, const float* v_scale,
+                                int num_pages, int Hkv, int page_size, int D,
+                                const void* q, int q_dtype,
+                                const int32_t* block_table, int max_pages,
+                                const int32_t* seq_lens, int batch, int n, int Hq,
+                                double scale, const uint64_t* tree_mask,
+                                const int32_t* seqs, int nseqs, double* out);
 
 #ifdef __cplusplus
 }

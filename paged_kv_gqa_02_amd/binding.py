@@ -56,7 +56,7 @@ class pa_plan(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m paged_kv_gqa_02_amd.build` (or __graft_entry__.build())")
+                          "`python paged_kv_gqa_02_amd/build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     st = ctypes.c_int
@@ -72,7 +72,9 @@ def _load():
         "paged_attn_verify": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32, i32,
                                    ctypes.c_float, vp, sz, vp]),
         "paged_attn_verify_timed": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32,
-                                         i32, ctypes.c_float, vp, sz, vp, vp, vp]),
+                                         i32, ctypes.c_float, vp, vp, sz, vp, vp, vp]),
+        "paged_attn_verify_tree": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32,
+                                        i32, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_validate": (st, [vp, vp, i32, vp, i32, i32, i32, vp]),
         "paged_attn_status_str": (ctypes.c_char_p, [st]),
         "paged_attn_last_error": (ctypes.c_char_p, []),
@@ -229,29 +231,58 @@ def _shapes(q, block_table, seq_lens):
 def paged_attn_verify(pool: Pool, q: torch.Tensor, out: torch.Tensor, block_table: torch.Tensor,
                       seq_lens: torch.Tensor, max_seq_len: int, scale: float,
                       workspace: Optional[torch.Tensor] = None, stream=None,
-                      ev_begin=None, ev_end=None) -> torch.Tensor:
-    """q, out: [batch][q_per_seq][Hq][128]; returns out."""
+                      ev_begin=None, ev_end=None, tree_mask: Optional[torch.Tensor] = None
+                      ) -> torch.Tensor:
+    """q, out: [batch][q_per_seq][Hq][128]; returns out.  With events (HipEvent)
+    or a tree mask this goes through paged_attn_verify_timed."""
     batch = _shapes(q, block_table, seq_lens)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
+    if tree_mask is not None and (tree_mask.shape != (batch, q.shape[1])
+                                  or tree_mask.element_size() != 8):
+        raise ValueError("tree_mask must be 64-bit [batch][q_per_seq]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (pool.handle, _dptr(q), _q_code(q), _dptr(out), _dptr(block_table),
+    head = (pool.handle, _dptr(q), _q_code(q), _dptr(out), _dptr(block_table),
             block_table.shape[1], _dptr(seq_lens), int(max_seq_len), batch, q.shape[1],
-            q.shape[2], float(scale), _dptr(workspace), ws_bytes, _stream(stream))
-    if ev_begin is None and ev_end is None:
-        _check(_lib.paged_attn_verify(*args), "paged_attn_verify")
+            q.shape[2], float(scale))
+    if ev_begin is None and ev_end is None and tree_mask is None:
+        _check(_lib.paged_attn_verify(*head, _dptr(workspace), ws_bytes, _stream(stream)),
+               "paged_attn_verify")
     else:
         hb = ev_begin.handle if ev_begin is not None else None
         he = ev_end.handle if ev_end is not None else None
-        _check(_lib.paged_attn_verify_timed(*args, hb, he), "paged_attn_verify_timed")
+        _check(_lib.paged_attn_verify_timed(*head, _dptr(tree_mask), _dptr(workspace), ws_bytes,
+                                            _stream(stream), hb, he),
+               "paged_attn_verify_timed")
+    return out
+
+
+def paged_attn_verify_tree(pool: Pool, q: torch.Tensor, out: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                           scale: float, tree_mask: torch.Tensor,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Draft-tree verification; tree_mask: [batch][q_per_seq] uint64 ancestor masks
+    (a torch.int64 / torch.uint64 device tensor holding the bit patterns)."""
+    batch = _shapes(q, block_table, seq_lens)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if tree_mask.shape != (batch, q.shape[1]) or tree_mask.element_size() != 8:
+        raise ValueError("tree_mask must be 64-bit [batch][q_per_seq]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attn_verify_tree(pool.handle, _dptr(q), _q_code(q), _dptr(out),
+                                       _dptr(block_table), block_table.shape[1], _dptr(seq_lens),
+                                       int(max_seq_len), batch, q.shape[1], q.shape[2],
+                                       float(scale), _dptr(tree_mask), _dptr(workspace),
+                                       ws_bytes, _stream(stream)),
+           "paged_attn_verify_tree")
     return out
 
 
 def paged_attn_verify_timed(pool, q, out, block_table, seq_lens, max_seq_len, scale,
-                            ev_begin, ev_end, workspace=None, stream=None):
+                            ev_begin, ev_end, workspace=None, stream=None, tree_mask=None):
     return paged_attn_verify(pool, q, out, block_table, seq_lens, max_seq_len, scale,
                              workspace=workspace, stream=stream, ev_begin=ev_begin,
-                             ev_end=ev_end)
+                             ev_end=ev_end, tree_mask=tree_mask)
 
 
 def paged_attn_decode(pool: Pool, q: torch.Tensor, out: torch.Tensor, block_table: torch.Tensor,

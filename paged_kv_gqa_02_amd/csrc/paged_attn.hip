@@ -81,6 +81,7 @@ struct Args {
     void* out;
     const int32_t* block_table;
     const int32_t* seq_lens;
+    const uint64_t* tree_mask; // [B][n] ancestor masks of a draft tree, or null (causal)
     float* part_acc;       // [B][n][Hq][num_splits][128]
     float* part_ml;        // [B][n][Hq][num_splits][2]  (max in log2 units, sum)
     int64_t page_stride;   // elements from one page to the next (Hkv * 16 * 128)
@@ -480,6 +481,17 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
         load_q(qf[nt], qrow, valid, g);
         qi[nt] = valid ? i : -1;
     }
+    // draft-tree verification: row i sees tree token j iff bit j of its mask
+    uint64_t tmask[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) tmask[nt] = ~uint64_t(0);
+    if (a.tree_mask) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint64_t mk = a.tree_mask[(int64_t)b * a.n + max(qi[nt], 0)];
+            tmask[nt] = qi[nt] >= 0 ? mk : ~uint64_t(0);
+        }
+    }
 
     // lengths are clamped to what the block table can describe, and page ids
     // to the pool, so that arrays breaking the contract give wrong numbers
@@ -491,6 +503,9 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     const int pg1 = min(pg0 + a.part_pages, npages);
     const int rows_here = min(RT, a.rows - row0);
     const int first_limit = L - a.n;          // row 0 sees tokens 0 .. L - n
+    // first token that some row may not see: L - n + 1 for the causal chain,
+    // L - n (the root) under a tree mask
+    const int mask_from = a.tree_mask ? first_limit : first_limit + 1;
 
     // per-row visibility limits (padding rows see every live token)
     int lim[NT];
@@ -513,7 +528,7 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
 
     auto consume = [&](Page<KV>& pg, int j) {
         const int base = (pg0 + wave + j * W) * kPage;
-        const bool need_mask = base + kPage - 1 > first_limit;
+        const bool need_mask = base + kPage - 1 >= mask_from;
         VOps vo;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -522,9 +537,19 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
 #pragma unroll
             for (int v = 0; v < 4; ++v) s[v] = sv[v] * a.scale_log2;
             if (need_mask) {
+                if (a.tree_mask) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    s[v] = (base + 4 * g + v <= lim[nt]) ? s[v] : -INFINITY;
+                    for (int v = 0; v < 4; ++v) {
+                        const int tok = base + 4 * g + v;
+                        const bool vis = tok < L && (tok < first_limit ||
+                                         ((tmask[nt] >> (tok - first_limit)) & 1u));
+                        s[v] = vis ? s[v] : -INFINITY;
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        s[v] = (base + 4 * g + v <= lim[nt]) ? s[v] : -INFINITY;
+                }
             }
             const float mx = group_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
             const bool grow = mx > m[nt] + kRescaleSlack;
@@ -856,8 +881,8 @@ void launch_partition_nt(int nt, int waves, int prefetch, const Args& a, int gri
 pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
               const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
               int32_t max_seq_len, int32_t batch, int32_t n, int32_t hq, float scale,
-              void* workspace, size_t workspace_bytes, void* stream, void* ev_begin,
-              void* ev_end)
+              const uint64_t* tree_mask, void* workspace, size_t workspace_bytes, void* stream,
+              void* ev_begin, void* ev_end)
 {
     if (!pool) return fail(PA_ERR_INVALID_ARG, "null pool");
     if (!q || !out || !block_table || !seq_lens)
@@ -899,6 +924,7 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
     a.out = out;
     a.block_table = block_table;
     a.seq_lens = seq_lens;
+    a.tree_mask = tree_mask;
     a.part_acc = static_cast<float*>(workspace);
     a.part_ml = need ? reinterpret_cast<float*>(
                            static_cast<char*>(workspace) +
@@ -1016,7 +1042,8 @@ PA_API pa_status paged_attn_decode(const pa_pool* pool, const void* q, pa_dtype 
                                    size_t workspace_bytes, void* stream)
 {
     return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
-               1, num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr);
+               1, num_q_heads, scale, nullptr, workspace, workspace_bytes, stream, nullptr,
+               nullptr);
 }
 
 PA_API pa_status paged_attn_verify(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
@@ -1026,19 +1053,39 @@ PA_API pa_status paged_attn_verify(const pa_pool* pool, const void* q, pa_dtype 
                                    void* workspace, size_t workspace_bytes, void* stream)
 {
     return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
-               q_per_seq, num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr);
+               q_per_seq, num_q_heads, scale, nullptr, workspace, workspace_bytes, stream, nullptr,
+               nullptr);
 }
 
 PA_API pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q_dtype,
                                          void* out, const int32_t* block_table,
                                          int32_t max_pages_per_seq, const int32_t* seq_lens,
                                          int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
-                                         int32_t num_q_heads, float scale, void* workspace,
+                                         int32_t num_q_heads, float scale,
+                                         const uint64_t* tree_mask, void* workspace,
                                          size_t workspace_bytes, void* stream, void* ev_begin,
                                          void* ev_end)
 {
+    if (tree_mask && q_per_seq > 64)
+        return fail(PA_ERR_UNSUPPORTED, "draft trees have at most 64 nodes");
     return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
-               q_per_seq, num_q_heads, scale, workspace, workspace_bytes, stream, ev_begin, ev_end);
+               q_per_seq, num_q_heads, scale, tree_mask, workspace, workspace_bytes, stream,
+               ev_begin, ev_end);
+}
+
+PA_API pa_status paged_attn_verify_tree(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                                        void* out, const int32_t* block_table,
+                                        int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                        int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                        int32_t num_q_heads, float scale,
+                                        const uint64_t* tree_mask, void* workspace,
+                                        size_t workspace_bytes, void* stream)
+{
+    if (!tree_mask) return fail(PA_ERR_INVALID_ARG, "null tree_mask");
+    if (q_per_seq > 64) return fail(PA_ERR_UNSUPPORTED, "draft trees have at most 64 nodes");
+    return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
+               q_per_seq, num_q_heads, scale, tree_mask, workspace, workspace_bytes, stream,
+               nullptr, nullptr);
 }
 
 PA_API pa_status paged_attn_validate(const pa_pool* pool, const int32_t* block_table,

@@ -43,7 +43,7 @@ def run_gpu(pa, case, partition_pages=0, dev=None, label="", waves=0, prefetch=0
     out = torch.empty_like(d.q)
     ws = pa.workspace_for(pool, d.q, case.max_seq_len)
     pa.paged_attn_verify(pool, d.q, out, d.block_table, d.seq_lens, case.max_seq_len,
-                         case.scale, ws)
+                         case.scale, ws, tree_mask=d.tree_mask)
     torch.cuda.synchronize()
     return to_numpy_f64(out)
 
@@ -51,7 +51,8 @@ def run_gpu(pa, case, partition_pages=0, dev=None, label="", waves=0, prefetch=0
 def run_oracle(case, seqs=None):
     return oracle.paged_attention(case.k_pool, case.v_pool, case.kv_dtype, case.q, case.q_dtype,
                                   case.block_table, case.seq_lens, case.q_per_seq, case.scale,
-                                  seqs=seqs, k_scale=case.k_scale, v_scale=case.v_scale)
+                                  seqs=seqs, k_scale=case.k_scale, v_scale=case.v_scale,
+                                  tree_mask=case.tree_mask)
 
 
 def check(gpu, ref, kv_dtype, what):
@@ -329,7 +330,54 @@ def sampled(case):
     return sorted(idx)
 
 
-@pytest.mark.parametrize("name", ["decode8b", "ragged", "verify", "fp8long"])
+# ----------------------------------------------------------------------------
+# draft-tree verification
+# ----------------------------------------------------------------------------
+def with_tree(case, seed):
+    rng = np.random.default_rng(seed)
+    case.tree_mask = np.stack([W.random_tree(rng, case.q_per_seq)[1] for _ in range(case.batch)])
+    return case
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("n", [5, 16, 64])
+def test_tree_verify_matches_oracle(pa, kv, n):
+    case = with_tree(small_case(kv, n, 32, 8, [n, n + 17, 300, 1000], seed=200 + n), 300 + n)
+    ref = run_oracle(case)
+    dev = to_device(case)
+    for part in (0, 3):
+        check(run_gpu(pa, case, part, dev=dev, label="tree"), ref, kv, f"tree n={n} part={part}")
+
+
+@pytest.mark.parametrize("n", [5, 16])
+def test_chain_tree_equals_causal_verify_bitwise(pa, n):
+    case = small_case("bf16", n, 32, 8, [4101, 77, n], seed=210 + n)
+    dev = to_device(case)
+    causal = run_gpu(pa, case, dev=dev, label="causal")
+    case.tree_mask = np.stack([W.chain_tree(n)] * case.batch)
+    chain = run_gpu(pa, case, label="chain tree")
+    assert (chain == causal).all()
+
+
+def test_tree_entry_point_and_limits(pa):
+    case = with_tree(small_case("bf16", 7, 8, 2, [100, 40], seed=220), 221)
+    d = to_device(case)
+    pool = pa.paged_attn_create_pool(d.k, d.v)
+    out = torch.empty_like(d.q)
+    ws = pa.workspace_for(pool, d.q, case.max_seq_len)
+    pa.paged_attn_verify_tree(pool, d.q, out, d.block_table, d.seq_lens, case.max_seq_len,
+                              case.scale, d.tree_mask, ws)
+    torch.cuda.synchronize()
+    check(to_numpy_f64(out), run_oracle(case), "bf16", "verify_tree entry point")
+    big = small_case("bf16", 65, 8, 2, [100], seed=222)
+    db = to_device(big)
+    with pytest.raises(pa.PagedAttnError):
+        pa.paged_attn_verify_tree(pool, db.q, torch.empty_like(db.q), db.block_table,
+                                  db.seq_lens, big.max_seq_len, big.scale,
+                                  torch.zeros((1, 65), dtype=torch.int64, device="cuda"))
+
+
+@pytest.mark.parametrize("name", ["decode8b", "ragged", "verify", "fp8long", "tree"])
 def test_workload_native_dtype(pa, name):
     case = W.workload(name)
     gpu = run_gpu(pa, case)
@@ -337,7 +385,7 @@ def test_workload_native_dtype(pa, name):
     check(gpu[seqs], run_oracle(case, seqs), case.kv_dtype, f"{name} sampled {seqs}")
 
 
-@pytest.mark.parametrize("name", ["decode8b", "ragged", "verify", "fp8long"])
+@pytest.mark.parametrize("name", ["decode8b", "ragged", "verify", "fp8long", "tree"])
 def test_workload_fp32_structure(pa, name):
     """Same shapes and layout in fp32: pins gather, masks and splits at 1e-5."""
     case = W.workload(name, kv_dtype="f32", q_dtype="f32")

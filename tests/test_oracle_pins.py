@@ -419,3 +419,64 @@ def test_paged_rejects_out_of_range_page():
     with pytest.raises(ValueError):
         oracle.paged_attention(case.k_pool, case.v_pool, "f32", case.q, "f32", tab,
                                case.seq_lens, 1, 1.0)
+
+
+# ----------------------------------------------------------------------------
+# draft-tree verification
+# ----------------------------------------------------------------------------
+def test_chain_tree_is_the_causal_verify():
+    L, n, hq, hkv, d = 60, 6, 8, 2, 16
+    q, k, v = _rand_qkv(40, L, n, hq, hkv, d)
+    assert (oracle.attention_tree(q, k, v, 0.3, W.chain_tree(n)) ==
+            oracle.attention(q, k, v, 0.3)).all()
+
+
+@pytest.mark.parametrize("n", [2, 7, 16, 64])
+def test_tree_node_equals_decode_along_its_path(n):
+    """Each node's output is plain decode over the context plus its ancestor path."""
+    L, hq, hkv, d = 40 + n, 4, 2, 16
+    rng = _rng(41 + n)
+    q, k, v = _rand_qkv(42 + n, L, n, hq, hkv, d)
+    _, masks = W.random_tree(rng, n)
+    out = oracle.attention_tree(q, k, v, 0.25, masks)
+    ctx = L - n
+    for i in range(n):
+        path = list(range(ctx)) + [ctx + j for j in W.ancestors(masks, i)]
+        dec = oracle.attention(q[i:i + 1], k[path], v[path], 0.25)
+        assert (dec[0] == out[i]).all()
+
+
+def test_star_tree_rows_see_root_and_self():
+    L, n, hq, hkv, d = 30, 5, 2, 1, 8
+    q, k, v = _rand_qkv(43, L, n, hq, hkv, d)
+    masks = np.array([1] + [1 | (1 << i) for i in range(1, n)], dtype=np.uint64)
+    out = oracle.attention_tree(q, k, v, 0.5, masks)
+    for i in range(1, n):
+        path = list(range(L - n)) + [L - n, L - n + i]
+        assert (oracle.attention(q[i:i + 1], k[path], v[path], 0.5)[0] == out[i]).all()
+
+
+def test_tree_rejects_too_many_nodes_and_blind_rows():
+    q, k, v = _rand_qkv(44, 70, 65, 2, 1, 8)
+    with pytest.raises(ValueError):
+        oracle.attention_tree(q, k, v, 1.0, np.ones(65, dtype=np.uint64))
+    q, k, v = _rand_qkv(45, 3, 3, 2, 1, 8)            # no context: row 1 sees nothing
+    with pytest.raises(ValueError):
+        oracle.attention_tree(q, k, v, 1.0, np.array([1, 0, 4], dtype=np.uint64))
+
+
+def test_paged_tree_matches_contiguous_tree():
+    n = 9
+    rng = _rng(46)
+    lens = [50, 9, 80]
+    hq, hkv, d = 8, 2, 16
+    kc = [rng.standard_normal((L, hkv, d)).astype(np.float32) for L in lens]
+    vc = [rng.standard_normal((L, hkv, d)).astype(np.float32) for L in lens]
+    tabs = [[3, 0, 7, 1], [5], [2, 4, 6, 8, 9]]
+    kp, vp = _scatter(kc, vc, tabs, 10)
+    q = rng.standard_normal((3, n, hq, d)).astype(np.float32)
+    masks = np.stack([W.random_tree(rng, n)[1] for _ in range(3)])
+    got = oracle.paged_attention(kp, vp, "f32", q, "f32", _table(tabs), lens, n, 0.3,
+                                 tree_mask=masks)
+    for b in range(3):
+        assert (got[b] == oracle.attention_tree(q[b], kc[b], vc[b], 0.3, masks[b])).all()

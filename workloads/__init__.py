@@ -180,6 +180,39 @@ def fragmented_tables(rng: np.random.Generator, seq_lens, slack: float = 1.25,
 
 
 # ----------------------------------------------------------------------------
+# draft trees
+# ----------------------------------------------------------------------------
+def chain_tree(n: int) -> np.ndarray:
+    """Ancestor masks of a chain of n drafts (the causal verify): row i sees rows 0..i."""
+    return np.array([(1 << (i + 1)) - 1 for i in range(n)], dtype=np.uint64)
+
+
+def random_tree(rng: np.random.Generator, n: int):
+    """A seeded random draft tree in topological order.
+
+    Node 0 is the root (the last accepted token); node i >= 1 hangs under a
+    parent drawn uniformly from 0 .. i-1.  Returns (parents, masks) with
+    masks[i] = the ancestors of node i and node i itself, as bits.
+    """
+    if not 1 <= n <= 64:
+        raise ValueError("trees of 1..64 nodes")
+    parents = np.full(n, -1, dtype=np.int64)
+    masks = np.zeros(n, dtype=np.uint64)
+    masks[0] = 1
+    for i in range(1, n):
+        p = int(rng.integers(0, i))
+        parents[i] = p
+        masks[i] = masks[p] | np.uint64(1 << i)
+    return parents, masks
+
+
+def ancestors(masks: np.ndarray, i: int):
+    """Indices of the tree rows node i sees, in row order."""
+    m = int(masks[i])
+    return [j for j in range(64) if (m >> j) & 1]
+
+
+# ----------------------------------------------------------------------------
 # cases
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass
@@ -203,6 +236,7 @@ class Case:
     k_scale: Optional[np.ndarray] = None   # [num_pages][Hkv] float32 (fp8)
     v_scale: Optional[np.ndarray] = None
     seed: int = 0
+    tree_mask: Optional[np.ndarray] = None  # [B][q_per_seq] uint64 draft-tree ancestor masks
 
     @property
     def max_seq_len(self) -> int:
@@ -343,7 +377,7 @@ def ragged_lengths(rng: np.random.Generator, batch: int = 240) -> np.ndarray:
     return (prompt + gen).astype(np.int32)
 
 
-WORKLOADS = ("tiny", "decode8b", "ragged", "verify", "fp8long")
+WORKLOADS = ("tiny", "decode8b", "ragged", "verify", "fp8long", "tree")
 
 
 def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] = None,
@@ -355,6 +389,8 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
     ragged    B240, 32/8 heads, ctx = U{128..1024} + {50|400}, fragmented pool, bf16
     verify    B8, 5 query rows (K = 4 drafts), 32/8 heads, ctx 4096 + 5, bf16
     fp8long   B4, 64/8 heads, ctx 32768, E4M3 K/V with per-(page, head) scales, bf16 Q
+    tree      B8, 32/8 heads, a seeded random 16-node draft tree per sequence after a
+              4096-token context (draft-tree verification), bf16
     """
     idx = WORKLOADS.index(name)
     s = BASE_SEED + idx if seed is None else seed
@@ -387,4 +423,13 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
         return make_case(name, batch=4, q_per_seq=1, num_q_heads=64, num_kv_heads=8,
                          seq_lens=[32768] * 4, kv_dtype=kv, q_dtype=qd, seed=s,
                          poison=poison)
+    if name == "tree":
+        kv, qd = kv_dtype or "bf16", q_dtype or "bf16"
+        n = 16
+        case = make_case(name, batch=8, q_per_seq=n, num_q_heads=32, num_kv_heads=8,
+                         seq_lens=[4096 + n] * 8, kv_dtype=kv, q_dtype=qd, seed=s,
+                         poison=poison)
+        rng = np.random.default_rng(s + 1)
+        case.tree_mask = np.stack([random_tree(rng, n)[1] for _ in range(case.batch)])
+        return case
     raise ValueError(name)

@@ -17,6 +17,7 @@ class DeviceCase:
     seq_lens: torch.Tensor
     k_scale: Optional[torch.Tensor]
     v_scale: Optional[torch.Tensor]
+    tree_mask: Optional[torch.Tensor] = None
 
 
 def tensor(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
@@ -30,10 +31,12 @@ def tensor(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
 
 
 def to_device(case, device="cuda") -> DeviceCase:
+    tm = getattr(case, "tree_mask", None)
     return DeviceCase(k=tensor(case.k_pool, device), v=tensor(case.v_pool, device),
                       q=tensor(case.q, device), block_table=tensor(case.block_table, device),
                       seq_lens=tensor(case.seq_lens, device),
-                      k_scale=tensor(case.k_scale, device), v_scale=tensor(case.v_scale, device))
+                      k_scale=tensor(case.k_scale, device), v_scale=tensor(case.v_scale, device),
+                      tree_mask=None if tm is None else tensor(tm.view(np.int64), device))
 
 
 def to_numpy_f64(t: torch.Tensor) -> np.ndarray:

@@ -55,6 +55,11 @@ def _load():
         lib.oracle_paged_attention_tree.restype = i
         lib.oracle_paged_attention_tree.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, i, vp, i,
                                                     vp, i, i, i, ctypes.c_double, vp, vp, i, vp]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_append_kv.restype = i
+        lib.oracle_append_kv.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, vp, i, vp, i, vp,
+                                         i, i]
         lib.oracle_paged_attention.restype = i
         lib.oracle_paged_attention.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, i, vp, i,
                                                vp, i, i, i, ctypes.c_double, vp, i, vp]
@@ -161,3 +166,38 @@ def paged_attention(k_pool, v_pool, kv_dtype: str, q, q_dtype: str, block_table,
     if rc != 0:
         raise ValueError(f"oracle_paged_attention rejected its arguments (code {rc})")
     return out
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 byte (ties to the even code, saturating at 448)."""
+    return int(_load().oracle_e4m3_encode(float(x)))
+
+
+def append_kv(k_pool, v_pool, kv_dtype: str, k_new, v_new, src_dtype: str, block_table,
+              seq_lens, n_new: int, k_scale=None, v_scale=None):
+    """KV append / quantize-on-write (see oracle_append_kv in oracle.h).
+
+    Works on copies: returns (k_pool, v_pool, k_scale, v_scale) after the
+    append.  k_new / v_new: [batch][n_new][Hkv][D] float32 or bf16 bits.
+    """
+    kp = np.array(k_pool, copy=True, order="C")
+    vp = np.array(v_pool, copy=True, order="C")
+    ks = vs = None
+    if kv_dtype == "fp8":
+        ks = np.array(k_scale, dtype=np.float32, copy=True)
+        vs = np.array(v_scale, dtype=np.float32, copy=True)
+    kn = np.ascontiguousarray(k_new)
+    vn = np.ascontiguousarray(v_new)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    num_pages, hkv, page_size, d = vp.shape
+    batch = lens.shape[0]
+    if kn.shape != (batch, n_new, hkv, d) or vn.shape != kn.shape or bt.shape[0] != batch:
+        raise ValueError("shape mismatch")
+    rc = _load().oracle_append_kv(_ptr(kp), _ptr(vp), _CODES[kv_dtype], _ptr(ks), _ptr(vs),
+                                  num_pages, hkv, page_size, d, _ptr(kn), _ptr(vn),
+                                  _CODES[src_dtype], _ptr(bt), bt.shape[1], _ptr(lens), batch,
+                                  n_new)
+    if rc != 0:
+        raise ValueError(f"oracle_append_kv rejected its arguments (code {rc})")
+    return kp, vp, ks, vs

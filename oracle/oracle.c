@@ -247,3 +247,142 @@ int oracle_paged_attention(const void* k_pool, const void* v_pool, int kv_dtype,
                                        Hkv, page_size, D, q, q_dtype, block_table, max_pages,
                                        seq_lens, batch, n, Hq, scale, NULL, seqs, nseqs, out);
 }
+
+/* ------------------------------------------------------------------------ */
+/* KV append                                                                  */
+/* ------------------------------------------------------------------------ */
+
+uint8_t oracle_e4m3_encode(double x)
+{
+    if (isnan(x))
+        return 0x7F;
+    const double a = fabs(x);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int code = 0; code <= 0x7E; ++code) {       /* every finite magnitude */
+        const double err = fabs(oracle_e4m3_value((uint8_t)code) - a);
+        if (err < best_err || (err == best_err && (code & 1) == 0)) {
+            best = code;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+/* bfloat16 bits nearest to a binary32 value (ties to even); NaN -> 0x7FC0 */
+static uint16_t to_bf16(float f)
+{
+    if (isnan(f))
+        return 0x7FC0;
+    /* candidates: truncate toward zero and the next pattern up in magnitude */
+    uint32_t w;
+    memcpy(&w, &f, sizeof w);
+    const uint16_t lo = (uint16_t)(w >> 16);
+    const uint16_t hi = (uint16_t)(lo + 1);
+    const double dl = fabs(oracle_bf16_value(lo) - (double)f);
+    const double dh = fabs(oracle_bf16_value(hi) - (double)f);
+    if (dl < dh || (dl == dh && (lo & 1) == 0))
+        return lo;
+    return hi;
+}
+
+static float source_value(const void* base, int code, size_t idx)
+{
+    return (float)element(base, code, idx);
+}
+
+int oracle_append_kv(void* k_pool, void* v_pool, int kv_dtype, float* k_scale, float* v_scale,
+                     int num_pages, int Hkv, int page_size, int D,
+                     const void* k_new, const void* v_new, int src_dtype,
+                     const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                     int batch, int n_new)
+{
+    if (!k_pool || !v_pool || !k_new || !v_new || !block_table || !seq_lens)
+        return ORACLE_BAD_ARG;
+    if (kv_dtype != ORACLE_F32 && kv_dtype != ORACLE_BF16 && kv_dtype != ORACLE_E4M3)
+        return ORACLE_BAD_ARG;
+    if (src_dtype != ORACLE_F32 && src_dtype != ORACLE_BF16)
+        return ORACLE_BAD_ARG;
+    if (kv_dtype == ORACLE_F32 && src_dtype != ORACLE_F32)
+        return ORACLE_BAD_ARG;
+    if (kv_dtype == ORACLE_E4M3 && (!k_scale || !v_scale))
+        return ORACLE_BAD_ARG;
+    if (num_pages < 1 || Hkv < 1 || page_size < 1 || D < 1 || max_pages < 1 || batch < 1 ||
+        n_new < 1)
+        return ORACLE_BAD_ARG;
+    const int x = 16 / element_bytes(kv_dtype);
+    if (D % x != 0)
+        return ORACLE_BAD_ARG;
+
+    for (int b = 0; b < batch; ++b) {
+        const int L = seq_lens[b];
+        if (L < n_new || L > page_size * max_pages)
+            return ORACLE_BAD_TABLE;
+        const int first = L - n_new;
+        for (int p = first / page_size; p <= (L - 1) / page_size; ++p) {
+            const int page = block_table[(size_t)b * max_pages + p];
+            if (page < 0 || page >= num_pages)
+                return ORACLE_BAD_TABLE;
+            const int s0 = p * page_size;                         /* first token of the page */
+            const int lo = first > s0 ? first - s0 : 0;           /* first new slot */
+            const int hi = (L - s0 < page_size) ? L - s0 : page_size;   /* one past the last */
+            for (int hk = 0; hk < Hkv; ++hk) {
+                const size_t slab = ((size_t)page * Hkv + hk) * page_size * D;
+                for (int which = 0; which < 2; ++which) {          /* 0: K, 1: V */
+                    void* pool = which ? v_pool : k_pool;
+                    const void* src = which ? v_new : k_new;
+                    float* scales = which ? v_scale : k_scale;
+                    /* slab index of (slot, d) */
+                    #define IDX(slot, d) (which ? slab + (size_t)(slot) * D + (d) \
+                        : slab + ((size_t)((d) / x) * page_size + (slot)) * x + (d) % x)
+                    #define SRC(slot, d) ((((size_t)b * n_new + (s0 + (slot) - first)) * Hkv + hk) \
+                        * D + (d))
+                    if (kv_dtype != ORACLE_E4M3) {
+                        for (int slot = lo; slot < hi; ++slot)
+                            for (int d = 0; d < D; ++d) {
+                                const float v = source_value(src, src_dtype, SRC(slot, d));
+                                if (kv_dtype == ORACLE_F32)
+                                    ((float*)pool)[IDX(slot, d)] = v;
+                                else
+                                    ((uint16_t*)pool)[IDX(slot, d)] = to_bf16(v);
+                            }
+                        continue;
+                    }
+                    uint8_t* bytes = (uint8_t*)pool;
+                    float amax = 0.0f;
+                    for (int slot = lo; slot < hi; ++slot)
+                        for (int d = 0; d < D; ++d) {
+                            const float v = fabsf(source_value(src, src_dtype, SRC(slot, d)));
+                            if (v > amax)
+                                amax = v;
+                        }
+                    const float cand = amax / 448.0f;
+                    float* sc = &scales[(size_t)page * Hkv + hk];
+                    float scale;
+                    if (lo == 0) {                                  /* no earlier live slot */
+                        scale = amax > 0.0f ? cand : 1.0f;
+                    } else {
+                        const float old = *sc;
+                        scale = cand > old ? cand : old;
+                        if (scale != old)
+                            for (int slot = 0; slot < lo; ++slot)
+                                for (int d = 0; d < D; ++d) {
+                                    const size_t i = IDX(slot, d);
+                                    const float val = (float)oracle_e4m3_value(bytes[i]) * old;
+                                    bytes[i] = oracle_e4m3_encode((double)(val / scale));
+                                }
+                    }
+                    for (int slot = lo; slot < hi; ++slot)
+                        for (int d = 0; d < D; ++d) {
+                            const float v = source_value(src, src_dtype, SRC(slot, d));
+                            bytes[IDX(slot, d)] = oracle_e4m3_encode((double)(v / scale));
+                        }
+                    *sc = scale;
+                    #undef IDX
+                    #undef SRC
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}

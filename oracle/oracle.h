@@ -117,6 +117,36 @@ int oracle_paged_attention_tree(const void* k_pool, const void* v_pool, int kv_d
                                 double scale, const uint64_t* tree_mask,
                                 const int32_t* seqs, int nseqs, double* out);
 
+/* Nearest E4M3 byte to x (ties to the even code), saturating at +-448; the
+ * search runs over every finite code.  NaN gives 0x7F. */
+uint8_t oracle_e4m3_encode(double x);
+
+/*
+ * KV append (quantize-on-write), the step before attention in a decode loop:
+ * writes the n_new newest tokens of every sequence (positions L - n_new .. L-1,
+ * L = seq_lens[b], which counts them) into the pool, in its layouts (K chunked,
+ * V token-major; see oracle_paged_attention).
+ *   k_new, v_new [batch][n_new][Hkv][D] source values, float32 or bf16 bits
+ *   f32 / bf16 pools: the value rounded to the pool format (round to nearest even)
+ *   E4M3 pools, per (page, kv head), K and V separately, all arithmetic in
+ *   binary32 (the precision the quantised code is decided in):
+ *     a page none of whose earlier slots are live gets
+ *       scale = absmax(new values in it) / 448   (1 if that absmax is 0);
+ *     otherwise scale = max(old scale, absmax / 448), and if it grew every
+ *       earlier live byte b becomes encode(value(b) * old / scale);
+ *     each new value x becomes encode(x / scale).
+ * Sources: "Latency and cost in production" §10.8.2 (q = round(x / scale) +
+ * zp, zp = 0 when symmetric, §10.8.3), §10.12.2 and "Batching, speculative
+ * decoding, paged attention" §5.3.7 (a request's blocks fill one token at a
+ * time, a new block when the last is full).
+ * Returns ORACLE_BAD_TABLE for a needed page id out of range or L < n_new.
+ */
+int oracle_append_kv(void* k_pool, void* v_pool, int kv_dtype, float* k_scale, float* v_scale,
+                     int num_pages, int Hkv, int page_size, int D,
+                     const void* k_new, const void* v_new, int src_dtype,
+                     const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                     int batch, int n_new);
+
 #ifdef __cplusplus
 }
 #endif

@@ -480,3 +480,119 @@ def test_paged_tree_matches_contiguous_tree():
                                  tree_mask=masks)
     for b in range(3):
         assert (got[b] == oracle.attention_tree(q[b], kc[b], vc[b], 0.3, masks[b])).all()
+
+
+# ----------------------------------------------------------------------------
+# KV append (quantize-on-write)
+# ----------------------------------------------------------------------------
+def test_e4m3_encode_is_nearest_with_ties_to_even():
+    codes, vals = _e4m3_table()
+    for x in [0.0, 1.0625, 1.1875, 447.9, 448.0, 470.0, 1e9, 2.0 ** -10, 0.75 * 2.0 ** -9]:
+        for sgn in (1, -1):
+            byte = oracle.e4m3_encode(sgn * x)
+            assert byte == W.e4m3_bytes(np.array([sgn * x]))[0]
+    assert oracle.e4m3_encode(float("nan")) == 0x7F
+
+
+def _append_case(kv, lens, n_new, seed, src="f32", num_pages=None):
+    qd = "f32" if kv == "f32" else "bf16"
+    case = W.make_case("app", batch=len(lens), q_per_seq=1, num_q_heads=4, num_kv_heads=2,
+                       seq_lens=lens, kv_dtype=kv, q_dtype=qd, seed=seed,
+                       num_pages=num_pages)
+    kn, vn = W.append_inputs(case, n_new, src, seed + 1)
+    return case, kn, vn
+
+
+def _append(case, kn, vn, src, n_new):
+    return oracle.append_kv(case.k_pool, case.v_pool, case.kv_dtype, kn, vn, src,
+                            case.block_table, case.seq_lens, n_new, case.k_scale, case.v_scale)
+
+
+@pytest.mark.parametrize("kv,src", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16")])
+def test_append_writes_rounded_values_where_attention_reads_them(kv, src):
+    lens, n_new = [37, 16, 5], 5
+    case, kn, vn = _append_case(kv, lens, n_new, 50, src)
+    kp, vp, _, _ = _append(case, kn, vn, src, n_new)
+    ktok = W.k_from_pool(kp)
+    srcf = lambda a: a if src == "f32" else (a.astype(np.uint32) << 16).view(np.float32)
+    want = lambda a: srcf(a) if kv == "f32" else W.bf16_bits(srcf(a))
+    for b, L in enumerate(lens):
+        for j in range(n_new):
+            t = L - n_new + j
+            page, slot = case.block_table[b, t // 16], t % 16
+            assert (ktok[page, :, slot] == want(kn[b, j])).all()
+            assert (vp[page, :, slot] == want(vn[b, j])).all()
+    # older tokens and other pages untouched
+    for b, L in enumerate(lens):
+        for t in range(L - n_new):
+            page, slot = case.block_table[b, t // 16], t % 16
+            assert (vp[page, :, slot] == case.v_pool[page, :, slot]).all() or np.isnan(
+                case.v_pool[page, :, slot]).all() if kv == "f32" else True
+
+
+def test_append_into_fresh_fp8_page_spans_the_range():
+    # a page whose first slot is new: scale = absmax / 448 and the largest value codes 448
+    lens, n_new = [16, 32], 16
+    case, kn, vn = _append_case("fp8", lens, n_new, 51, "f32")
+    kp, vp, ks, vs = _append(case, kn, vn, "f32", n_new)
+    for b in range(2):
+        page = case.block_table[b, lens[b] // 16 - 1]
+        for hk in range(2):
+            amax = np.abs(kn[b, :, hk]).max()
+            assert ks[page, hk] == np.float32(amax) / np.float32(448)
+            slab = W.k_from_pool(kp)[page, hk]
+            assert (slab & 0x7F).max() == 0x7E
+            dec = np.vectorize(oracle.e4m3_value)(slab) * float(ks[page, hk])
+            step = np.abs(kn[b, :, hk]) * 2.0 ** -4 + float(ks[page, hk]) * 2.0 ** -10
+            assert (np.abs(dec - kn[b, :, hk]) <= step).all()   # RNE: half an E4M3 step
+
+
+def test_append_one_at_a_time_equals_bulk_when_the_first_token_holds_the_max():
+    lens, n_new = [16], 16
+    case, kn, vn = _append_case("fp8", lens, n_new, 52, "f32")
+    kn[:, 0] *= 10.0                                  # token 0 holds each head's absmax
+    vn[:, 0] *= 10.0
+    bulk = _append(case, kn, vn, "f32", n_new)
+    state = (case.k_pool, case.v_pool, case.k_scale, case.v_scale)
+    for j in range(n_new):
+        state = oracle.append_kv(state[0], state[1], "fp8", kn[:, j:j + 1], vn[:, j:j + 1],
+                                 "f32", case.block_table, np.array([j + 1], np.int32), 1,
+                                 state[2], state[3])
+    for a, b2 in zip(bulk, state):
+        assert (a == b2).all()
+
+
+def test_append_requantizes_older_tokens_when_the_scale_grows():
+    lens, n_new = [20], 3                             # page 1 holds tokens 16..19
+    case, kn, vn = _append_case("fp8", lens, n_new, 53, "f32")
+    page = case.block_table[0, 1]
+    old_scale = case.k_scale[page, 0]
+    old_byte = W.k_from_pool(case.k_pool)[page, 0, 0]      # token 16: live, not rewritten
+    kn[0, 0, 0] = 1000.0 * old_scale                        # new absmax >> old range
+    kp, _, ks, _ = _append(case, kn, vn, "f32", n_new)
+    new_scale = ks[page, 0]
+    assert new_scale == np.float32(np.abs(kn[0, :, 0]).max()) / np.float32(448)
+    for d in (0, 5, 127):
+        val = np.float32(oracle.e4m3_value(old_byte[d])) * old_scale
+        assert W.k_from_pool(kp)[page, 0, 0, d] == oracle.e4m3_encode(float(val / new_scale))
+    # a smaller new token leaves the scale and the older bytes alone
+    case2, kn2, vn2 = _append_case("fp8", lens, n_new, 54, "f32")
+    kn2 *= 0.0
+    kp2, _, ks2, _ = _append(case2, kn2, vn2, "f32", n_new)
+    assert (ks2[page] == case2.k_scale[page]).all()
+    assert (W.k_from_pool(kp2)[page, :, 0] == W.k_from_pool(case2.k_pool)[page, :, 0]).all()
+
+
+def test_append_then_attention_equals_attention_on_the_source_values():
+    lens, n_new = [40, 18], 6
+    case, kn, vn = _append_case("f32", lens, n_new, 55, "f32")
+    kp, vp, _, _ = _append(case, kn, vn, "f32", n_new)
+    full = oracle.paged_attention(kp, vp, "f32", case.q, "f32", case.block_table,
+                                  case.seq_lens, 1, case.scale)
+    ktok = W.k_from_pool(case.k_pool)
+    for b, L in enumerate(lens):
+        kc = np.stack([ktok[case.block_table[b, t // 16], :, t % 16] for t in range(L)])
+        vc = np.stack([case.v_pool[case.block_table[b, t // 16], :, t % 16] for t in range(L)])
+        kc[L - n_new:] = kn[b]
+        vc[L - n_new:] = vn[b]
+        assert (oracle.attention(case.q[b], kc, vc, case.scale) == full[b]).all()

@@ -433,3 +433,18 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
         case.tree_mask = np.stack([random_tree(rng, n)[1] for _ in range(case.batch)])
         return case
     raise ValueError(name)
+
+
+# ----------------------------------------------------------------------------
+# KV append inputs
+# ----------------------------------------------------------------------------
+def append_inputs(case: Case, n_new: int, src_dtype: str, seed: int, spread: float = 1.0):
+    """Source K/V for the n_new newest tokens of every sequence of `case`:
+    [batch][n_new][Hkv][D], N(0, spread^2) as float32 or bf16 bits."""
+    rng = np.random.default_rng(seed)
+    shape = (case.batch, n_new, case.num_kv_heads, case.head_dim)
+    k = (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(spread))
+    v = (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(spread))
+    if src_dtype == "bf16":
+        return bf16_bits(k), bf16_bits(v)
+    return k, v

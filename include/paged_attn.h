@@ -88,10 +88,11 @@ typedef struct pa_pool_desc {
     int32_t num_kv_heads;
     int32_t head_dim;         /* must be 128 */
     pa_dtype kv_dtype;
-    const void* k;            /* [num_pages][num_kv_heads][128/x][16][x], x = 16 / elem size */
-    const void* v;            /* [num_pages][num_kv_heads][16][128] */
-    const float* k_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
-    const float* v_scale;     /* [num_pages][num_kv_heads], fp8 only, else NULL */
+    /* pool arrays: read by the attention calls, written only by paged_attn_append_kv */
+    void* k;                  /* [num_pages][num_kv_heads][128/x][16][x], x = 16 / elem size */
+    void* v;                  /* [num_pages][num_kv_heads][16][128] */
+    float* k_scale;           /* [num_pages][num_kv_heads], fp8 only, else NULL */
+    float* v_scale;           /* [num_pages][num_kv_heads], fp8 only, else NULL */
     int32_t partition_pages;  /* split-K partition length in pages; 0 = chosen per call */
     int32_t waves;            /* tuning: waves per workgroup (4 or 8); 0 = automatic */
     int32_t prefetch;         /* tuning: pages held in registers per wave (2..6, at most 4 with
@@ -183,6 +184,28 @@ pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q
                                   int32_t num_q_heads, float scale, const uint64_t* tree_mask,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   void* ev_begin, void* ev_end);
+
+/* KV append (quantize-on-write), the step before attention in a decode or
+ * verify pass: writes the n_new newest tokens of each sequence (positions
+ * L - n_new .. L - 1, L = seq_lens[b], which counts them) into the pool, in its
+ * layouts.  k_new, v_new: device [batch][n_new][num_kv_heads][128] of src_dtype
+ * (PA_F32 or PA_BF16; an f32 pool takes f32), 16-byte aligned.
+ *   f32 / bf16 pools: the value rounded to the pool format (nearest even).
+ *   fp8 pools, per (page, kv head), K and V separately, in binary32
+ *   ("Latency and cost in production" §10.8.2-§10.8.3: q = round(x / scale),
+ *   zero-point 0):
+ *     a page none of whose earlier slots are live takes
+ *       scale = absmax(its new values) / 448 (1 if that absmax is 0);
+ *     otherwise scale = max(old scale, absmax / 448), and when it grows every
+ *       earlier live byte b is re-encoded as encode(value(b) * old / scale);
+ *     each new value x is stored as encode(x / scale): the nearest E4M3 value,
+ *     ties to even, saturating at +-448.
+ * The pages for the new positions must be in the block table.  Calls that
+ * touch the same pages must not overlap. */
+pa_status paged_attn_append_kv(const pa_pool* pool, const void* k_new, const void* v_new,
+                               pa_dtype src_dtype, const int32_t* block_table,
+                               int32_t max_pages_per_seq, const int32_t* seq_lens,
+                               int32_t batch, int32_t n_new, void* stream);
 
 /* Debug check of the device-array contract: copies block_table and seq_lens
  * to the host (synchronously, on `stream`) and returns PA_ERR_CONTRACT if a

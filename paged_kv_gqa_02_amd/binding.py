@@ -75,6 +75,7 @@ def _load():
                                          i32, ctypes.c_float, vp, vp, sz, vp, vp, vp]),
         "paged_attn_verify_tree": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32,
                                         i32, ctypes.c_float, vp, vp, sz, vp]),
+        "paged_attn_append_kv": (st, [vp, vp, vp, ctypes.c_int, vp, i32, vp, i32, i32, vp]),
         "paged_attn_validate": (st, [vp, vp, i32, vp, i32, i32, i32, vp]),
         "paged_attn_status_str": (ctypes.c_char_p, [st]),
         "paged_attn_last_error": (ctypes.c_char_p, []),
@@ -303,6 +304,21 @@ def paged_attn_decode(pool: Pool, q: torch.Tensor, out: torch.Tensor, block_tabl
                                   _dptr(workspace), ws_bytes, _stream(stream)),
            "paged_attn_decode")
     return out
+
+
+def paged_attn_append_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor,
+                         block_table: torch.Tensor, seq_lens: torch.Tensor, stream=None):
+    """Write the n_new newest tokens ([batch][n_new][Hkv][128], float32 or bfloat16)
+    of every sequence into the pool (fp8 pools: quantize-on-write)."""
+    if k_new.shape != v_new.shape or k_new.dim() != 4 or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must both be [batch][n_new][Hkv][128]")
+    batch, n_new = k_new.shape[0], k_new.shape[1]
+    if block_table.dim() != 2 or block_table.shape[0] != batch or seq_lens.shape != (batch,):
+        raise ValueError("block_table / seq_lens must have one row per sequence")
+    _check(_lib.paged_attn_append_kv(pool.handle, _dptr(k_new), _dptr(v_new), _q_code(k_new),
+                                     _dptr(block_table), block_table.shape[1], _dptr(seq_lens),
+                                     batch, n_new, _stream(stream)),
+           "paged_attn_append_kv")
 
 
 def paged_attn_validate(pool: Pool, block_table: torch.Tensor, seq_lens: torch.Tensor,

@@ -717,6 +717,182 @@ __global__ __launch_bounds__(kReduceThreads) void paged_attn_reduce(Args a)
 }
 
 // ---------------------------------------------------------------------------
+// KV append (quantize-on-write): the n_new newest tokens of every sequence are
+// written into their pages ("Latency and cost in production" §10.12.2: a
+// request's blocks fill one token at a time; §10.8.2-§10.8.3: q =
+// round(x / scale) with zero-point 0).  One wave per (sequence, kv head); the
+// work unit is one 16-byte chunk of one token row (K chunked, V token-major).
+// fp8 pages: scale = absmax / 448 over the new values of a page none of whose
+// earlier slots are live (1 if 0); otherwise max(old, absmax / 448), and the
+// earlier live bytes are re-encoded when it grows.  All in binary32.
+// ---------------------------------------------------------------------------
+struct AppendArgs {
+    void* k;
+    void* v;
+    float* k_scale;
+    float* v_scale;
+    const void* k_new;     // [B][n_new][Hkv][128]
+    const void* v_new;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int64_t page_stride;   // elements from one page to the next (Hkv * 16 * 128)
+    int32_t num_pages;
+    int32_t max_pages;
+    int32_t hkv;
+    int32_t n_new;
+};
+
+// E4M3 value of a byte, exactly (sign, 4-bit exponent with bias 7, 3-bit mantissa)
+__device__ __forceinline__ float e4m3_to_float(uint32_t byte)
+{
+    const uint32_t e = (byte >> 3) & 0xF, m = byte & 0x7;
+    const float mag = e == 0 ? (float)m * 0.001953125f                       // m * 2^-9
+                             : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (byte & 0x80) ? -mag : mag;
+}
+
+// Nearest E4M3 byte to x, ties to even, saturating at +-448
+__device__ __forceinline__ uint32_t float_to_e4m3(float x)
+{
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80;
+    const float a = fabsf(x);
+    uint32_t code;
+    if (!(a < 448.0f)) {
+        code = 0x7E;
+    } else if (a < 0.015625f) {                                  // below 2^-6: steps of 2^-9
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        const int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // a in [2^e, 2^(e+1))
+        const uint32_t steps = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
+        code = min((uint32_t)((e + 7) << 3) + steps - 8u, 0x7Eu);
+    }
+    return sign | code;
+}
+
+template <bool SRC_BF16>
+__device__ __forceinline__ float src_value(const void* base, int64_t idx)
+{
+    if constexpr (SRC_BF16)
+        return bf16_float(static_cast<const uint16_t*>(base)[idx]);
+    else
+        return static_cast<const float*>(base)[idx];
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+template <int KV, bool SRC_BF16>
+__global__ __launch_bounds__(kWave) void paged_attn_append(AppendArgs a)
+{
+    constexpr int esz = KV == KV_F32 ? 4 : KV == KV_BF16 ? 2 : 1;
+    constexpr int X = 16 / esz;                     // elements per 16-byte chunk
+    constexpr int C = kHeadDim / X;                 // chunks per token row
+    const int lane = threadIdx.x;
+    const int kh = blockIdx.x % a.hkv;
+    const int b = blockIdx.x / a.hkv;
+    const int L = min(a.seq_lens[b], a.max_pages * kPage);
+    const int first = L - a.n_new;
+    if (first < 0) return;
+    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+
+    for (int p = first / kPage; p <= (L - 1) / kPage; ++p) {
+        const int phys = min(max(bt_row[p], 0), a.num_pages - 1);
+        const int s0 = p * kPage;
+        const int lo = max(first - s0, 0);          // first new slot of this page
+        const int hi = min(L - s0, kPage);          // one past the last
+        const int64_t slab = (int64_t)phys * a.page_stride + (int64_t)kh * kSlab;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            uint8_t* pool = static_cast<uint8_t*>(which ? a.v : a.k) + slab * esz;
+            const void* src = which ? a.v_new : a.k_new;
+            // byte offset of chunk c of slot `slot` in this slab
+            auto at = [&](int slot, int c) -> int64_t {
+                return which ? (int64_t)(slot * kHeadDim + c * X) * esz
+                             : (int64_t)(c * kPage + slot) * 16;
+            };
+            auto src_idx = [&](int slot, int c) -> int64_t {
+                return (((int64_t)b * a.n_new + (s0 + slot - first)) * a.hkv + kh) * kHeadDim +
+                       c * X;
+            };
+            if constexpr (KV != KV_FP8) {
+                for (int e = lane; e < (hi - lo) * C; e += kWave) {
+                    const int slot = lo + e / C, c = e % C;
+                    const int64_t si = src_idx(slot, c);
+                    u32x4 w;
+                    if constexpr (KV == KV_F32) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            w[i] = __float_as_uint(src_value<SRC_BF16>(src, si + i));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            w[i] = bf16_bits(src_value<SRC_BF16>(src, si + 2 * i)) |
+                                   (bf16_bits(src_value<SRC_BF16>(src, si + 2 * i + 1)) << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(pool + at(slot, c)) = w;
+                }
+            } else {
+                float* scales = which ? a.v_scale : a.k_scale;
+                float amax = 0.f;
+                for (int e = lane; e < (hi - lo) * kHeadDim; e += kWave) {
+                    const int slot = lo + e / kHeadDim, d = e % kHeadDim;
+                    amax = fmaxf(amax, fabsf(src_value<SRC_BF16>(src, src_idx(slot, 0) + d)));
+                }
+                amax = wave_max(amax);
+                const float cand = amax / 448.0f;
+                const int64_t si = (int64_t)phys * a.hkv + kh;
+                float scale;
+                if (lo == 0) {
+                    scale = amax > 0.f ? cand : 1.0f;
+                } else {
+                    const float old = scales[si];
+                    scale = cand > old ? cand : old;
+                    if (scale != old) {
+                        // the page's earlier live bytes move to the larger scale
+                        for (int e = lane; e < lo * C; e += kWave) {
+                            const int slot = e / C, c = e % C;
+                            u32x4* ptr = reinterpret_cast<u32x4*>(pool + at(slot, c));
+                            u32x4 w = *ptr;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                uint32_t out = 0;
+#pragma unroll
+                                for (int k = 0; k < 4; ++k) {
+                                    const float val = e4m3_to_float((w[i] >> (8 * k)) & 0xFF) * old;
+                                    out |= float_to_e4m3(val / scale) << (8 * k);
+                                }
+                                w[i] = out;
+                            }
+                            *ptr = w;
+                        }
+                    }
+                }
+                for (int e = lane; e < (hi - lo) * C; e += kWave) {
+                    const int slot = lo + e / C, c = e % C;
+                    const int64_t sidx = src_idx(slot, c);
+                    u32x4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t out = 0;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            out |= float_to_e4m3(src_value<SRC_BF16>(src, sidx + 4 * i + k) / scale)
+                                   << (8 * k);
+                        w[i] = out;
+                    }
+                    *reinterpret_cast<u32x4*>(pool + at(slot, c)) = w;
+                }
+                if (lane == 0) scales[si] = scale;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 thread_local std::string g_last_error;
@@ -1086,6 +1262,59 @@ PA_API pa_status paged_attn_verify_tree(const pa_pool* pool, const void* q, pa_d
     return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
                q_per_seq, num_q_heads, scale, tree_mask, workspace, workspace_bytes, stream,
                nullptr, nullptr);
+}
+
+PA_API pa_status paged_attn_append_kv(const pa_pool* pool, const void* k_new, const void* v_new,
+                                      pa_dtype src_dtype, const int32_t* block_table,
+                                      int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                      int32_t batch, int32_t n_new, void* stream)
+{
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "null pool");
+    if (!k_new || !v_new || !block_table || !seq_lens)
+        return fail(PA_ERR_INVALID_ARG, "null k_new, v_new, block_table or seq_lens");
+    if (batch < 1 || n_new < 1 || max_pages_per_seq < 1)
+        return fail(PA_ERR_INVALID_ARG, "batch, n_new and max_pages_per_seq must be >= 1");
+    if (n_new > (int64_t)kPage * max_pages_per_seq)
+        return fail(PA_ERR_INVALID_ARG, "n_new exceeds 16 * max_pages_per_seq");
+    if (src_dtype != PA_F32 && src_dtype != PA_BF16)
+        return fail(PA_ERR_INVALID_ARG, "source values must be f32 or bf16");
+    const pa_pool_desc& d = pool->d;
+    if (d.kv_dtype == PA_F32 && src_dtype != PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "an f32 pool takes f32 source values");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+        return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    if ((int64_t)batch * d.num_kv_heads > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+    AppendArgs a;
+    a.k = d.k;
+    a.v = d.v;
+    a.k_scale = d.k_scale;
+    a.v_scale = d.v_scale;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.page_stride = (int64_t)d.num_kv_heads * kSlab;
+    a.num_pages = d.num_pages;
+    a.max_pages = max_pages_per_seq;
+    a.hkv = d.num_kv_heads;
+    a.n_new = n_new;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)(batch * d.num_kv_heads));
+    const bool bf = src_dtype == PA_BF16;
+    switch (d.kv_dtype) {
+    case PA_F32: hipLaunchKernelGGL((paged_attn_append<KV_F32, false>), grid, dim3(kWave), 0, st, a); break;
+    case PA_BF16:
+        if (bf) hipLaunchKernelGGL((paged_attn_append<KV_BF16, true>), grid, dim3(kWave), 0, st, a);
+        else hipLaunchKernelGGL((paged_attn_append<KV_BF16, false>), grid, dim3(kWave), 0, st, a);
+        break;
+    default:
+        if (bf) hipLaunchKernelGGL((paged_attn_append<KV_FP8, true>), grid, dim3(kWave), 0, st, a);
+        else hipLaunchKernelGGL((paged_attn_append<KV_FP8, false>), grid, dim3(kWave), 0, st, a);
+        break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    return PA_OK;
 }
 
 PA_API pa_status paged_attn_validate(const pa_pool* pool, const int32_t* block_table,

@@ -11,6 +11,12 @@ whose write-back would then compete with the timed kernel for HBM.
 
 Prints ONE JSON line (rank 0).  `value` is effective HBM GB/s: (K + V bytes of
 every token of every sequence, fp8 scales, Q, O) / mean call time.
+
+`--op append` instead times paged_attn_append_kv, the step before attention:
+the n_new newest tokens of every sequence of the workload (default: its query
+rows; `--n-new 256` is a prefill chunk) are written into the pool, quantised
+on write for fp8.  Its bytes are the source K/V read, the pool bytes written
+and, for fp8, every touched page scale read and written.
 """
 from __future__ import annotations
 
@@ -43,6 +49,8 @@ def parse():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--op", default="attention", choices=("attention", "append"))
+    ap.add_argument("--n-new", type=int, default=0, help="append: tokens per sequence")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a torch copy of 512 MiB ten times (scale for HBM counters)")
     return ap.parse_args()
@@ -92,6 +100,99 @@ def cpu_baseline(case, reps):
             "sample": f"whole batch ({case.batch} sequences, every head and row) x {reps} reps, "
                       f"median {t:.3f} s, float64 C oracle, one sequence per thread",
             "tokens_per_s": case.batch * case.q_per_seq / t}
+
+
+def append_bytes(case, n_new, src_dtype, seq_lens=None):
+    """Source K/V read + pool bytes written (+ fp8 scales of touched pages, read and
+    written) for the sequences with lengths `seq_lens` (default: the whole batch)."""
+    lens = (case.seq_lens if seq_lens is None else seq_lens).astype(np.int64)
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}
+    elems = len(lens) * n_new * case.num_kv_heads * case.head_dim
+    nbytes = 2 * elems * (esz[src_dtype] + esz[case.kv_dtype])
+    if case.kv_dtype == "fp8":
+        pages = (lens - 1) // W.PAGE_SIZE - (lens - n_new) // W.PAGE_SIZE + 1
+        nbytes += 2 * 2 * 4 * int(pages.sum()) * case.num_kv_heads
+    return nbytes
+
+
+def cpu_append_baseline(case, kn, vn, src, n_new, budget_s=10.0):
+    """The oracle's append over a bounded prefix of the batch, one thread."""
+    import oracle
+
+    def run(k):
+        t0 = time.perf_counter()
+        oracle.append_kv(case.k_pool, case.v_pool, case.kv_dtype, kn[:k], vn[:k], src,
+                         case.block_table[:k], case.seq_lens[:k], n_new, case.k_scale,
+                         case.v_scale)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    k = int(max(1, min(case.batch, budget_s / max(t1, 1e-6))))
+    t = run(k) if k > 1 else t1
+    log(f"cpu append baseline: {k} sequences in {t:.2f} s")
+    return {"value": append_bytes(case, n_new, src, case.seq_lens[:k]) / t / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{k} of {case.batch} sequences, n_new={n_new}, one call of the C oracle "
+                      f"(which also copies the pool), {t:.2f} s",
+            "tokens_per_s": k * n_new / t}
+
+
+def bench_append(args, torch, pa, case, dev, pool, flush_caches, stream):
+    from workloads.device import tensor
+
+    n_new = args.n_new or case.q_per_seq
+    if n_new > int(case.seq_lens.min()):
+        sys.exit(f"bench.py: n_new={n_new} exceeds the shortest sequence of {case.name}")
+    src = "f32" if case.kv_dtype == "f32" else "bf16"
+    kn, vn = W.append_inputs(case, n_new, src, 20261202)
+    dk, dv = tensor(kn, "cuda"), tensor(vn, "cuda")
+
+    def call():
+        pa.paged_attn_append_kv(pool, dk, dv, dev.block_table, dev.seq_lens)
+
+    for _ in range(args.warmup):
+        flush_caches()
+        call()
+    torch.cuda.synchronize()
+    # The flush kernel in front of every call keeps the queue busy while the
+    # host enqueues the begin event and the launch, so the events bracket the
+    # append kernel and its dispatch.
+    evs = [(pa.HipEvent(), pa.HipEvent()) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        flush_caches()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_ms(e1) for e0, e1 in evs])
+    nbytes = append_bytes(case, n_new, src)
+    sec = float(ms.mean()) / 1e3
+    gbs = nbytes / sec / 1e9
+    log(f"append: {ms.mean() * 1e3:.2f} us per call, {gbs:.1f} GB/s")
+    result = {
+        "metric": "KV append (quantize-on-write) effective HBM GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 source", "f32": "f32"}[case.kv_dtype],
+        "data": "synthetic (seeded N(0,1) sources, shuffled page pool)",
+        "config": {"workload": f"append into {case.name}", "batch": case.batch, "n_new": n_new,
+                   "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+                   "kv_dtype": case.kv_dtype, "src_dtype": src, "bytes_per_call": nbytes},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(case.batch * n_new / sec, 1),
+        "call_us": {"mean": round(float(ms.mean()) * 1e3, 2),
+                    "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                    "p50": round(float(np.percentile(ms, 50)) * 1e3, 2),
+                    "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "paged_attn_append", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "kernel_us_mean": round(sec * 1e6, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_append_baseline(case, kn, vn, src, n_new)
+    print(json.dumps(result), flush=True)
 
 
 def copy_calibration(torch):
@@ -146,6 +247,10 @@ def main():
     def flush_caches():
         if flush is not None:
             flush.sum(dtype=torch.float32)
+
+    if args.op == "append":
+        bench_append(args, torch, pa, case, dev, pool, flush_caches, stream)
+        return
 
     log(f"plan {plan}; warmup {args.warmup}")
     for _ in range(args.warmup):

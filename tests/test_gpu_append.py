@@ -117,6 +117,38 @@ def test_append_workloads(pa, name, n_new, src):
                        oracle_append(case, kn, vn, src, n_new))
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_prefill_chunk(pa, kv):
+    """A prefill chunk: 256 new tokens per sequence, starting mid-page, 17 pages each."""
+    lens = [256 + 7, 1000, 256, 777, 300, 512 + 15, 999, 260]
+    case = W.make_case("chunk", batch=len(lens), q_per_seq=1, num_q_heads=32, num_kv_heads=8,
+                       seq_lens=lens, kv_dtype=kv, q_dtype="bf16", seed=450)
+    kn, vn = W.append_inputs(case, 256, "bf16", 451)
+    assert_pools_equal(gpu_append(pa, case, kn, vn, 256),
+                       oracle_append(case, kn, vn, "bf16", 256))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_is_invariant_to_page_placement(pa, kv):
+    """Renumbering the physical pages (data moved with them) renumbers the result."""
+    lens, n_new = [70, 33, 129], 20
+    case = W.make_case("perm", batch=3, q_per_seq=1, num_q_heads=4, num_kv_heads=2,
+                       seq_lens=lens, kv_dtype=kv, q_dtype="bf16", seed=460)
+    kn, vn = W.append_inputs(case, n_new, "bf16", 461)
+    base = gpu_append(pa, case, kn, vn, n_new)
+    perm = np.random.default_rng(462).permutation(case.num_pages)    # new id of page j
+    moved = W.Case(**{**case.__dict__})
+    inv = np.argsort(perm)
+    moved.k_pool, moved.v_pool = case.k_pool[inv], case.v_pool[inv]
+    if case.k_scale is not None:
+        moved.k_scale, moved.v_scale = case.k_scale[inv], case.v_scale[inv]
+    moved.block_table = perm[case.block_table].astype(np.int32)
+    got = gpu_append(pa, moved, kn, vn, n_new)
+    for g, w in zip(got, base):
+        if w is not None:
+            assert same_bits(np.ascontiguousarray(g[perm]), w)
+
+
 def test_append_rejects_bad_arguments(pa):
     case = W.make_case("bad", batch=1, q_per_seq=1, num_q_heads=2, num_kv_heads=1,
                        seq_lens=[20], kv_dtype="f32", q_dtype="f32", seed=440)

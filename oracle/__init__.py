@@ -60,6 +60,8 @@ def _load():
         lib.oracle_append_kv.restype = i
         lib.oracle_append_kv.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, vp, i, vp, i, vp,
                                          i, i]
+        lib.oracle_rejection_sample.restype = i
+        lib.oracle_rejection_sample.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp]
         lib.oracle_paged_attention.restype = i
         lib.oracle_paged_attention.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, i, vp, i,
                                                vp, i, i, i, ctypes.c_double, vp, i, vp]
@@ -201,3 +203,26 @@ def append_kv(k_pool, v_pool, kv_dtype: str, k_new, v_new, src_dtype: str, block
     if rc != 0:
         raise ValueError(f"oracle_append_kv rejected its arguments (code {rc})")
     return kp, vp, ks, vs
+
+
+def rejection_sample(p, q, draft, u_accept, u_sample):
+    """Speculative-sampling acceptance (see oracle_rejection_sample in oracle.h).
+
+    p [B][K+1][V], q [B][K][V] float32; draft [B][K] int32; u_accept [B][K],
+    u_sample [B] float32 in [0, 1).  Returns (tokens [B][K+1] int32 with -1
+    after the sampled token, accepted [B] int32).
+    """
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    batch, k1, vocab = p.shape
+    k = k1 - 1
+    q = np.ascontiguousarray(q, dtype=np.float32).reshape(batch, k, vocab)
+    draft = np.ascontiguousarray(draft, dtype=np.int32).reshape(batch, k)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(batch, k)
+    us = np.ascontiguousarray(u_sample, dtype=np.float32).reshape(batch)
+    tokens = np.empty((batch, k + 1), dtype=np.int32)
+    accepted = np.empty(batch, dtype=np.int32)
+    rc = _load().oracle_rejection_sample(_ptr(p), _ptr(q), _ptr(draft), _ptr(ua), _ptr(us),
+                                         batch, k, vocab, _ptr(tokens), _ptr(accepted))
+    if rc != 0:
+        raise ValueError(f"oracle_rejection_sample rejected its arguments (code {rc})")
+    return tokens, accepted

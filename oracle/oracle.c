@@ -386,3 +386,67 @@ int oracle_append_kv(void* k_pool, void* v_pool, int kv_dtype, float* k_scale, f
     }
     return ORACLE_OK;
 }
+
+/* inverse-CDF draw from non-negative weights w[0..V): the smallest j whose
+ * running (left-to-right, binary64) sum exceeds u * total; -1 if total is 0 */
+static int32_t draw(const double* w, int V, float u)
+{
+    double total = 0.0;
+    for (int j = 0; j < V; ++j) total += w[j];
+    if (!(total > 0.0)) return -1;
+    const double target = (double)u * total;
+    double run = 0.0;
+    for (int j = 0; j < V; ++j) {
+        run += w[j];
+        if (run > target) return j;
+    }
+    return -1;   /* unreachable: run ends at total > target */
+}
+
+int oracle_rejection_sample(const float* p, const float* q, const int32_t* draft,
+                            const float* u_accept, const float* u_sample,
+                            int batch, int K, int V, int32_t* tokens, int32_t* accepted)
+{
+    if (batch < 0 || K < 0 || V < 1) return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < (size_t)batch * K; ++i)
+        if (draft[i] < 0 || draft[i] >= V) return ORACLE_BAD_ARG;
+    double* w = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!w) return ORACLE_NO_MEMORY;
+    for (int b = 0; b < batch; ++b) {
+        const float* pb = p + (size_t)b * (K + 1) * V;
+        const float* qb = q + (size_t)b * K * V;
+        int32_t* out = tokens + (size_t)b * (K + 1);
+        /* acceptance tests, in order, up to the first rejection */
+        int r = 0;
+        while (r < K) {
+            const int x = draft[(size_t)b * K + r];
+            const double px = pb[(size_t)r * V + x], qx = qb[(size_t)r * V + x];
+            if (!((double)u_accept[(size_t)b * K + r] * qx < px)) break;
+            out[r] = x;
+            ++r;
+        }
+        accepted[b] = r;
+        /* the one sampled token: residual after a rejection, else the bonus */
+        const float* pr = pb + (size_t)r * V;
+        int32_t tok;
+        if (r < K) {
+            const float* qr = qb + (size_t)r * V;
+            for (int j = 0; j < V; ++j) {
+                const double d = (double)pr[j] - (double)qr[j];
+                w[j] = d > 0.0 ? d : 0.0;
+            }
+            tok = draw(w, V, u_sample[b]);
+            if (tok < 0) {                      /* no residual mass: p itself */
+                for (int j = 0; j < V; ++j) w[j] = pr[j];
+                tok = draw(w, V, u_sample[b]);
+            }
+        } else {
+            for (int j = 0; j < V; ++j) w[j] = pr[j];
+            tok = draw(w, V, u_sample[b]);
+        }
+        out[r] = tok;
+        for (int i = r + 1; i <= K; ++i) out[i] = -1;
+    }
+    free(w);
+    return ORACLE_OK;
+}

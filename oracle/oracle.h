@@ -147,6 +147,37 @@ int oracle_append_kv(void* k_pool, void* v_pool, int kv_dtype, float* k_scale, f
                      const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                      int batch, int n_new);
 
+/*
+ * Speculative-sampling acceptance (rejection sampling), the step after the
+ * verify pass, for each sequence b of a batch:
+ *   p         [batch][K+1][V] target probabilities (float32), one row per
+ *             verify position (rows need not sum to exactly 1)
+ *   q         [batch][K][V]   draft probabilities (float32)
+ *   draft     [batch][K]      the draft tokens, in [0, V)
+ *   u_accept  [batch][K]      uniforms in [0, 1), one per acceptance test
+ *   u_sample  [batch]         a uniform in [0, 1) for the one token sampled
+ *   tokens    [batch][K+1]    out: accepted drafts, the sampled token, then -1
+ *   accepted  [batch]         out: number of accepted drafts (0 .. K)
+ * Draft i (x = draft[b][i]) is accepted with probability min(1, p(x)/q(x)):
+ * iff u_accept[b][i] * q[b][i][x] < p[b][i][x] (exact in binary64, because
+ * both factors have 24-bit significands).  Tests run i = 0, 1, ... and stop
+ * at the first rejection, at position r.  The one sampled token comes from
+ *   w = max(0, p[b][r] - q[b][r])   after a rejection at r (the residual;
+ *       if it sums to 0, w = p[b][r]),
+ *   w = p[b][K]                     when all K drafts are accepted (the bonus),
+ * by inverse CDF: the smallest j with w_0 + ... + w_j > u_sample[b] * sum(w),
+ * every sum taken left to right in binary64.  A row with no mass gives -1.
+ * Sources: "Latency and cost in production" §10.6.2 (accept if p >= q, else
+ * with probability p/q; on rejection sample from norm(max(0, p - q)); bonus
+ * token when every draft passes) and "Speculative decoding principles"
+ * (7.2.1), acceptance rule (a uniform u is drawn and the draft passes iff
+ * u < p/q) and residual distribution.
+ * Returns ORACLE_BAD_ARG for K < 0, V < 1 or a draft token outside [0, V).
+ */
+int oracle_rejection_sample(const float* p, const float* q, const int32_t* draft,
+                            const float* u_accept, const float* u_sample,
+                            int batch, int K, int V, int32_t* tokens, int32_t* accepted);
+
 #ifdef __cplusplus
 }
 #endif

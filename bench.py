@@ -17,6 +17,13 @@ the n_new newest tokens of every sequence of the workload (default: its query
 rows; `--n-new 256` is a prefill chunk) are written into the pool, quantised
 on write for fp8.  Its bytes are the source K/V read, the pool bytes written
 and, for fp8, every touched page scale read and written.
+
+`--op sample` times paged_attn_rejection_sample, the step after the verify
+pass: speculative-sampling acceptance for `--batch` sequences (default 64)
+with `--drafts` drafts (4) over a `--vocab` (128,256) vocabulary.  Its bytes
+are the probabilities the method must read given the outcome (the drafted
+tokens' p and q up to the first rejection, then the residual's p and q rows,
+or the bonus p row), the draft tokens and uniforms, and the outputs.
 """
 from __future__ import annotations
 
@@ -49,7 +56,10 @@ def parse():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
-    ap.add_argument("--op", default="attention", choices=("attention", "append"))
+    ap.add_argument("--op", default="attention", choices=("attention", "append", "sample"))
+    ap.add_argument("--batch", type=int, default=64, help="sample: sequences")
+    ap.add_argument("--drafts", type=int, default=4, help="sample: drafts per sequence")
+    ap.add_argument("--vocab", type=int, default=W.VOCAB_8B, help="sample: vocabulary size")
     ap.add_argument("--n-new", type=int, default=0, help="append: tokens per sequence")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a torch copy of 512 MiB ten times (scale for HBM counters)")
@@ -195,6 +205,86 @@ def bench_append(args, torch, pa, case, dev, pool, flush_caches, stream):
     print(json.dumps(result), flush=True)
 
 
+def sample_bytes(case, accepted):
+    """Bytes the acceptance must touch given the outcome (see the module doc)."""
+    k, v = case.num_drafts, case.vocab
+    acc = accepted.astype(np.int64)
+    tests = np.minimum(acc + 1, k)                     # acceptance tests actually run
+    rows = np.where(acc < k, 2 * v * 4, v * 4)         # residual p and q rows, or the bonus row
+    return int((tests * 16 + rows + 4 + (k + 1) * 4 + 4).sum())
+
+
+def bench_sample(args, torch, pa, flush_caches, stream):
+    log(f"generating sampler inputs B={args.batch} K={args.drafts} V={args.vocab}")
+    case = W.sampler_inputs(args.batch, args.drafts, args.vocab, 20261202)
+    k = case.num_drafts
+    dp = torch.from_numpy(case.p).cuda()
+    dq = torch.from_numpy(case.q).cuda() if k else None
+    dd = torch.from_numpy(case.draft).cuda() if k else None
+    dua = torch.from_numpy(case.u_accept).cuda() if k else None
+    dus = torch.from_numpy(case.u_sample).cuda()
+    tokens = torch.empty((case.batch, k + 1), dtype=torch.int32, device="cuda")
+    acc = torch.empty(case.batch, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, pa.paged_attn_rejection_sample_workspace_bytes(case.batch, case.vocab)),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        pa.paged_attn_rejection_sample(dp, dq, dd, dua, dus, tokens, acc, ws)
+
+    for _ in range(args.warmup):
+        flush_caches()
+        call()
+    torch.cuda.synchronize()
+    evs = [(pa.HipEvent(), pa.HipEvent()) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        flush_caches()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_ms(e1) for e0, e1 in evs])
+    accepted = acc.cpu().numpy()
+    nbytes = sample_bytes(case, accepted)
+    sec = float(ms.mean()) / 1e3
+    gbs = nbytes / sec / 1e9
+    log(f"sample: {ms.mean() * 1e3:.2f} us per call, {gbs:.1f} GB/s, "
+        f"mean accepted {accepted.mean():.2f}")
+    result = {
+        "metric": "speculative-sampling acceptance effective HBM GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 probabilities, f64 sums",
+        "data": "synthetic (seeded N(0, 3^2) target logits, draft = target + N(0, 0.5^2))",
+        "config": {"workload": f"acceptance B={case.batch} K={k} V={case.vocab}",
+                   "batch": case.batch, "num_drafts": k, "vocab": case.vocab,
+                   "mean_accepted": round(float(accepted.mean()), 4), "bytes_per_call": nbytes},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(float((accepted + 1).sum()) / sec, 1),
+        "call_us": {"mean": round(float(ms.mean()) * 1e3, 2),
+                    "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                    "p50": round(float(np.percentile(ms, 50)) * 1e3, 2),
+                    "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "spec_sample_chunks + spec_sample_pick",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel_us_mean": round(sec * 1e6, 2), "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        times = []
+        for _ in range(max(3, args.cpu_reps)):
+            t0 = time.perf_counter()
+            oracle.rejection_sample(case.p, case.q, case.draft, case.u_accept, case.u_sample)
+            times.append(time.perf_counter() - t0)
+        t = float(np.median(times))
+        result["cpu_baseline"] = {
+            "value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole batch, {len(times)} reps, median {t * 1e3:.2f} ms, one thread",
+            "tokens_per_s": float((accepted + 1).sum()) / t}
+    print(json.dumps(result), flush=True)
+
+
 def copy_calibration(torch):
     """A plain device copy of known size: reads and writes 512 MiB per launch."""
     n = 512 << 20
@@ -225,6 +315,19 @@ def main():
         copy_calibration(torch)
         return
 
+    flush = None
+    if not args.no_flush:
+        flush = torch.ones(FLUSH_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def flush_caches():
+        if flush is not None:
+            flush.sum(dtype=torch.float32)
+
+    if args.op == "sample":
+        bench_sample(args, torch, pa, flush_caches, stream)
+        return
+
     log(f"generating {args.workload}")
     case = W.workload(args.workload)
     dev = to_device(case)
@@ -234,19 +337,11 @@ def main():
                               case.max_seq_len)
     out = torch.empty_like(dev.q)
     ws = pa.workspace_for(pool, dev.q, case.max_seq_len)
-    flush = None
-    if not args.no_flush:
-        flush = torch.ones(FLUSH_BYTES // 2, dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
 
     def call(ev_begin=None, ev_end=None):
         pa.paged_attn_verify(pool, dev.q, out, dev.block_table, dev.seq_lens, case.max_seq_len,
                              case.scale, ws, ev_begin=ev_begin, ev_end=ev_end,
                              tree_mask=dev.tree_mask)
-
-    def flush_caches():
-        if flush is not None:
-            flush.sum(dtype=torch.float32)
 
     if args.op == "append":
         bench_append(args, torch, pa, case, dev, pool, flush_caches, stream)

@@ -207,6 +207,42 @@ pa_status paged_attn_append_kv(const pa_pool* pool, const void* k_new, const voi
                                int32_t max_pages_per_seq, const int32_t* seq_lens,
                                int32_t batch, int32_t n_new, void* stream);
 
+/* Speculative-sampling acceptance (rejection sampling), the step after the
+ * verify pass ("Latency and cost in production" §10.6.2; "Speculative
+ * decoding principles" 7.2.1, acceptance rule and residual distribution).
+ * All arrays are device memory owned by the caller:
+ *   p            [batch][num_drafts + 1][vocab] float32 target probabilities
+ *                (row r scores position r; the last row gives the bonus token)
+ *   q            [batch][num_drafts][vocab] float32 draft probabilities
+ *   draft        [batch][num_drafts] int32 draft tokens, in [0, vocab)
+ *   u_accept     [batch][num_drafts] float32 uniforms in [0, 1)
+ *   u_sample     [batch] float32 uniforms in [0, 1)
+ *   tokens       [batch][num_drafts + 1] int32 out: the accepted drafts, then
+ *                the sampled token, then -1
+ *   num_accepted [batch] int32 out
+ * Draft i (x = draft[b][i]) passes iff u_accept[b][i] * q[b][i][x] <
+ * p[b][i][x], evaluated exactly in binary64, i.e. with probability
+ * min(1, p/q); tests run in order and stop at the first rejection, at r.
+ * One token is then drawn with u = u_sample[b] from the weights
+ *   w = max(0, p[b][r] - q[b][r]) after a rejection (p[b][r] itself when that
+ *       residual is all zero), or w = p[b][num_drafts] when all drafts pass,
+ * as the first j at which the running binary64 sum of w exceeds u * sum(w).
+ * The running sum is taken in one fixed order (64-entry runs, then their
+ * totals, then 4096-entry chunk totals, each left to right), so it rises only
+ * on positive weights: a zero-weight token is never drawn.  A row with no
+ * mass gives token -1.  p and q rows must be finite and >= 0; a draft token
+ * outside [0, vocab) is clamped (the result is then unspecified).
+ * Limits: num_drafts <= 64, vocab <= 1,048,576, batch <= 65535.  Workspace:
+ * paged_attn_rejection_sample_workspace_bytes(batch, vocab) bytes (two
+ * binary64 per 4096-entry chunk of a row, then one int32, per sequence), 8-byte
+ * aligned, no initial contents.  Two kernels on `stream`; asynchronous. */
+size_t paged_attn_rejection_sample_workspace_bytes(int32_t batch, int32_t vocab);
+pa_status paged_attn_rejection_sample(const float* p, const float* q, const int32_t* draft,
+                                      const float* u_accept, const float* u_sample,
+                                      int32_t batch, int32_t num_drafts, int32_t vocab,
+                                      int32_t* tokens, int32_t* num_accepted,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Debug check of the device-array contract: copies block_table and seq_lens
  * to the host (synchronously, on `stream`) and returns PA_ERR_CONTRACT if a
  * length or a needed page id is out of range. */

@@ -77,6 +77,9 @@ def _load():
                                         i32, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_append_kv": (st, [vp, vp, vp, ctypes.c_int, vp, i32, vp, i32, i32, vp]),
         "paged_attn_validate": (st, [vp, vp, i32, vp, i32, i32, i32, vp]),
+        "paged_attn_rejection_sample_workspace_bytes": (sz, [i32, i32]),
+        "paged_attn_rejection_sample": (st, [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz,
+                                             vp]),
         "paged_attn_status_str": (ctypes.c_char_p, [st]),
         "paged_attn_last_error": (ctypes.c_char_p, []),
     }
@@ -327,6 +330,47 @@ def paged_attn_validate(pool: Pool, block_table: torch.Tensor, seq_lens: torch.T
     _check(_lib.paged_attn_validate(pool.handle, _dptr(block_table), block_table.shape[1],
                                     _dptr(seq_lens), int(max_seq_len), batch, q_per_seq,
                                     _stream(stream)), "paged_attn_validate")
+
+
+def paged_attn_rejection_sample_workspace_bytes(batch: int, vocab: int) -> int:
+    return int(_lib.paged_attn_rejection_sample_workspace_bytes(int(batch), int(vocab)))
+
+
+def paged_attn_rejection_sample(p: torch.Tensor, q: Optional[torch.Tensor],
+                                draft: Optional[torch.Tensor], u_accept: Optional[torch.Tensor],
+                                u_sample: torch.Tensor, tokens: Optional[torch.Tensor] = None,
+                                num_accepted: Optional[torch.Tensor] = None, workspace=None,
+                                stream=None):
+    """Speculative-sampling acceptance.  p [B][K+1][V], q [B][K][V] float32; draft
+    [B][K] int32; u_accept [B][K], u_sample [B] float32.  Returns (tokens [B][K+1],
+    num_accepted [B]) int32 device tensors (allocated here unless passed in)."""
+    if p.dim() != 3 or p.dtype != torch.float32:
+        raise ValueError("p must be float32 [batch][K+1][vocab]")
+    batch, k1, vocab = p.shape
+    k = k1 - 1
+    if k > 0:
+        if q is None or q.shape != (batch, k, vocab) or q.dtype != torch.float32:
+            raise ValueError("q must be float32 [batch][K][vocab]")
+        if draft is None or draft.shape != (batch, k) or draft.dtype != torch.int32:
+            raise ValueError("draft must be int32 [batch][K]")
+        if u_accept is None or u_accept.shape != (batch, k) or u_accept.dtype != torch.float32:
+            raise ValueError("u_accept must be float32 [batch][K]")
+    if u_sample.shape != (batch,) or u_sample.dtype != torch.float32:
+        raise ValueError("u_sample must be float32 [batch]")
+    if tokens is None:
+        tokens = torch.empty((batch, k1), dtype=torch.int32, device=p.device)
+    if num_accepted is None:
+        num_accepted = torch.empty((batch,), dtype=torch.int32, device=p.device)
+    ws_bytes = paged_attn_rejection_sample_workspace_bytes(batch, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=p.device)
+    kk = k > 0
+    _check(_lib.paged_attn_rejection_sample(
+        _dptr(p), _dptr(q) if kk else None, _dptr(draft) if kk else None,
+        _dptr(u_accept) if kk else None, _dptr(u_sample), batch, k, vocab, _dptr(tokens),
+        _dptr(num_accepted), _dptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "paged_attn_rejection_sample")
+    return tokens, num_accepted
 
 
 # ---------------------------------------------------------------------------

@@ -7,7 +7,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "paged_attn.hip")
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "spec_sample.hip")]
 LIB = os.path.join(PKG, "libpaged_attn.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -22,7 +22,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in res.stderr.splitlines() if noise not in x)

@@ -42,6 +42,7 @@
 #include <vector>
 
 #include "paged_attn.h"
+#include "status.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
@@ -908,19 +909,9 @@ __global__ __launch_bounds__(kWave) void paged_attn_append(AppendArgs a)
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-thread_local std::string g_last_error;
+pa_status fail(pa_status st, const char* what) { return pa_record_error(st, what); }
 
-pa_status fail(pa_status st, const char* what)
-{
-    g_last_error = what;
-    return st;
-}
-
-pa_status hip_fail(hipError_t e, const char* where)
-{
-    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
-    return PA_ERR_HIP;
-}
+pa_status hip_fail(hipError_t e, const char* where) { return pa_record_hip_error(e, where); }
 
 int cu_count()
 {
@@ -1381,6 +1372,20 @@ PA_API const char* paged_attn_status_str(pa_status status)
     case PA_ERR_CONTRACT: return "device array violates the contract";
     default: return "unknown status";
     }
+}
+
+static thread_local std::string g_last_error;
+
+pa_status pa_record_error(pa_status st, const char* what)
+{
+    g_last_error = what;
+    return st;
+}
+
+pa_status pa_record_hip_error(hipError_t e, const char* where)
+{
+    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    return PA_ERR_HIP;
 }
 
 PA_API const char* paged_attn_last_error(void) { return g_last_error.c_str(); }

@@ -147,3 +147,40 @@ def test_verify_rejects_before_launch(kw, status):
 
 def test_null_pool_rejected():
     assert _verify(None) == B.PA_ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------------------
+# speculative-sampling acceptance: host-side checks (return before any launch)
+# ----------------------------------------------------------------------------
+def _sample(p=0x40000, q=0x50000, draft=0x60000, ua=0x70000, us=0x80000, batch=4, k=4,
+            vocab=128256, tokens=0x90000, acc=0xA0000, ws=0xB0000, ws_bytes=1 << 20):
+    return LIB.paged_attn_rejection_sample(p, q, draft, ua, us, batch, k, vocab, tokens, acc, ws,
+                                           ws_bytes, None)
+
+
+def test_sample_workspace_bytes():
+    # two binary64 sums per 4096-entry chunk, then one int32 per sequence
+    assert pa.paged_attn_rejection_sample_workspace_bytes(64, 128256) == 64 * 32 * 16 + 64 * 4
+    assert pa.paged_attn_rejection_sample_workspace_bytes(1, 4096) == 16 + 4
+    assert pa.paged_attn_rejection_sample_workspace_bytes(1, 4097) == 32 + 4
+    assert pa.paged_attn_rejection_sample_workspace_bytes(0, 10) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=None), B.PA_ERR_INVALID_ARG),
+    (dict(us=None), B.PA_ERR_INVALID_ARG),
+    (dict(tokens=None), B.PA_ERR_INVALID_ARG),
+    (dict(q=None), B.PA_ERR_INVALID_ARG),                        # drafts but no q
+    (dict(batch=0), B.PA_ERR_INVALID_ARG),
+    (dict(vocab=0), B.PA_ERR_INVALID_ARG),
+    (dict(k=-1), B.PA_ERR_INVALID_ARG),
+    (dict(k=65), B.PA_ERR_UNSUPPORTED),
+    (dict(vocab=(1 << 20) + 1), B.PA_ERR_UNSUPPORTED),
+    (dict(batch=65536), B.PA_ERR_UNSUPPORTED),
+    (dict(ws=None), B.PA_ERR_WORKSPACE),
+    (dict(ws_bytes=64 * 32 * 16 - 1, batch=64), B.PA_ERR_WORKSPACE),
+    (dict(ws=0xB0004), B.PA_ERR_INVALID_ARG),                    # misaligned workspace
+])
+def test_sample_rejects_before_launch(kw, status):
+    assert _sample(**kw) == status
+    assert LIB.paged_attn_last_error()

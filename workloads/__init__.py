@@ -448,3 +448,73 @@ def append_inputs(case: Case, n_new: int, src_dtype: str, seed: int, spread: flo
     if src_dtype == "bf16":
         return bf16_bits(k), bf16_bits(v)
     return k, v
+
+
+# ----------------------------------------------------------------------------
+# speculative-sampling acceptance inputs
+# ----------------------------------------------------------------------------
+VOCAB_8B = 128256        # vocabulary of an 8B-class GQA model (the pages fix none)
+
+
+@dataclasses.dataclass
+class SamplerCase:
+    """Inputs of one acceptance call: p [B][K+1][V], q [B][K][V] float32 rows,
+    draft [B][K] int32 drawn from q, uniforms u_accept [B][K], u_sample [B]."""
+    p: np.ndarray
+    q: np.ndarray
+    draft: np.ndarray
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+
+    @property
+    def batch(self) -> int:
+        return self.p.shape[0]
+
+    @property
+    def num_drafts(self) -> int:
+        return self.p.shape[1] - 1
+
+    @property
+    def vocab(self) -> int:
+        return self.p.shape[2]
+
+
+def _softmax_rows(z: np.ndarray) -> np.ndarray:
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def _draw_rows(rows: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """One index per row of probabilities (the draft model's own sampling)."""
+    cdf = np.cumsum(rows.astype(np.float64), axis=-1)
+    idx = (cdf < (u * cdf[..., -1])[..., None]).sum(axis=-1)
+    return np.minimum(idx, rows.shape[-1] - 1).astype(np.int32)
+
+
+def sampler_inputs(batch: int, num_drafts: int, vocab: int, seed: int,
+                   temperature_logit_sd: float = 3.0, draft_noise_sd: float = 0.5,
+                   greedy: bool = False) -> SamplerCase:
+    """Target logits N(0, sd^2) per row; the draft's logits are the target's
+    plus N(0, noise^2) (a close but imperfect draft: at the defaults a draft
+    passes about 80 % of the time); p, q = softmax; draft
+    token i is drawn from q row i; uniforms in [0, 1) as float32.  greedy:
+    one-hot rows at the logits' argmax instead (temperature 0)."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((batch, num_drafts + 1, vocab), dtype=np.float32) * \
+        np.float32(temperature_logit_sd)
+    zq = z[:, :num_drafts] + rng.standard_normal((batch, num_drafts, vocab),
+                                                 dtype=np.float32) * np.float32(draft_noise_sd)
+    if greedy:
+        p = np.zeros_like(z)
+        np.put_along_axis(p, z.argmax(axis=-1)[..., None], 1.0, axis=-1)
+        q = np.zeros_like(zq)
+        np.put_along_axis(q, zq.argmax(axis=-1)[..., None], 1.0, axis=-1)
+    else:
+        p = _softmax_rows(z.astype(np.float64))
+        q = _softmax_rows(zq.astype(np.float64))
+    del z, zq
+    draft = _draw_rows(q, rng.random((batch, num_drafts)))
+    return SamplerCase(p=p, q=q.astype(np.float32), draft=draft,
+                       u_accept=rng.random((batch, num_drafts), dtype=np.float32),
+                       u_sample=rng.random(batch, dtype=np.float32))

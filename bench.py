@@ -66,6 +66,25 @@ def parse():
     return ap.parse_args()
 
 
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}   # dense; fp8 KV runs bf16 MFMA
+MFMA_RIDGE = 2500.0e12 / 8000.0e9                                  # FLOP per HBM byte, bf16
+
+
+def attention_flops(case):
+    """4 * head_dim multiply-adds-as-two-flops per (query head, visible key):
+    q.k and p * v.  Row i of a sequence sees L - n + i + 1 keys (draft trees:
+    the context plus the row's ancestors)."""
+    n = case.q_per_seq
+    keys = 0
+    for b, L in enumerate(case.seq_lens.astype(np.int64)):
+        if case.tree_mask is not None:
+            anc = sum(bin(int(m)).count("1") for m in case.tree_mask[b])
+            keys += n * (L - n) + anc
+        else:
+            keys += n * (L - n) + n * (n + 1) // 2
+    return 4 * case.head_dim * case.num_q_heads * int(keys)
+
+
 def measured_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the kernel source as it is now (else None)."""
@@ -385,11 +404,13 @@ def main():
         f"partition kernel {kern_ms.mean() * 1e3:.1f} us")
 
     nbytes = case.algorithmic_bytes()
+    flops = attention_flops(case)
     call_s = float(call_ms.mean()) / 1e3
     kern_s = float(kern_ms.mean()) / 1e3
     gbs = nbytes / call_s / 1e9
     achieved = nbytes / kern_s / 1e9
     rows = case.batch * case.q_per_seq
+    mfma_bound = flops / nbytes > MFMA_RIDGE
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -421,11 +442,27 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(case.name),
                      "kernel_us_mean": round(kern_s * 1e6, 2),
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "flops_per_launch": flops},
     }
+    if mfma_bound:
+        # above the MFMA ridge (chunked prefill): the contraction bounds the kernel
+        peak = PEAK_MFMA_TFLOPS[case.kv_dtype]
+        tflops = flops / kern_s / 1e12
+        result.update({
+            "metric": "chunked-prefill attention TFLOP/s (MFMA-bound)",
+            "value": round(flops / call_s / 1e12, 2), "unit": "TFLOP/s",
+            "pct_of_peak": round(100 * flops / call_s / 1e12 / peak, 2)})
+        result["roofline"].update({"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                                   "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                                   "hbm_gbs": round(achieved, 1)})
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_reps)
+        cpu = cpu_baseline(case, args.cpu_reps)
+        if mfma_bound:
+            sec = case.algorithmic_bytes() / (cpu["value"] * 1e9)
+            cpu.update({"value": flops / sec / 1e12, "unit": "TFLOP/s"})
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

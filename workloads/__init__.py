@@ -377,7 +377,7 @@ def ragged_lengths(rng: np.random.Generator, batch: int = 240) -> np.ndarray:
     return (prompt + gen).astype(np.int32)
 
 
-WORKLOADS = ("tiny", "decode8b", "ragged", "verify", "fp8long", "tree")
+WORKLOADS = ("tiny", "decode8b", "ragged", "verify", "fp8long", "tree", "prefill")
 
 
 def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] = None,
@@ -391,6 +391,8 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
     fp8long   B4, 64/8 heads, ctx 32768, E4M3 K/V with per-(page, head) scales, bf16 Q
     tree      B8, 32/8 heads, a seeded random 16-node draft tree per sequence after a
               4096-token context (draft-tree verification), bf16
+    prefill   B4, 32/8 heads, one 512-token prefill chunk per sequence after 1536, 1024,
+              512 and 0 earlier tokens (a 2048-token prompt in four chunks), bf16
     """
     idx = WORKLOADS.index(name)
     s = BASE_SEED + idx if seed is None else seed
@@ -432,6 +434,12 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
         rng = np.random.default_rng(s + 1)
         case.tree_mask = np.stack([random_tree(rng, n)[1] for _ in range(case.batch)])
         return case
+    if name == "prefill":
+        kv, qd = kv_dtype or "bf16", q_dtype or "bf16"
+        n = 512
+        return make_case(name, batch=4, q_per_seq=n, num_q_heads=32, num_kv_heads=8,
+                         seq_lens=[1536 + n, 1024 + n, 512 + n, n], kv_dtype=kv, q_dtype=qd,
+                         seed=s, poison=poison)
     raise ValueError(name)
 
 

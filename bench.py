@@ -85,19 +85,20 @@ def attention_flops(case):
     return 4 * case.head_dim * case.num_q_heads * int(keys)
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the kernel source as it is now (else None)."""
+def measured_traffic(key):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter runs (profiles/traffic.json), if they were taken on the kernel
+    source as it is now (else None)."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, "profiles", "traffic.json")
-    src = os.path.join(root, "paged_kv_gqa_02_amd", "csrc", "paged_attn.hip")
     try:
-        rec = json.load(open(path)).get(workload)
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except (OSError, ValueError):
+        rec = json.load(open(os.path.join(root, "profiles", "traffic.json"))).get(key)
+        if not rec:
+            return None
+        digest = hashlib.sha256(open(os.path.join(root, rec["source"]), "rb").read()).hexdigest()
+    except (OSError, ValueError, KeyError):
         return None
-    if not rec or rec.get("source_sha256") != digest:
+    if rec.get("source_sha256") != digest:
         return None
     return int(round(rec["traffic_bytes"]))
 
@@ -216,7 +217,7 @@ def bench_append(args, torch, pa, case, dev, pool, flush_caches, stream):
                     "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "paged_attn_append", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None, "kernel_us_mean": round(sec * 1e6, 2),
+                     "traffic": measured_traffic(f"append:{case.name}:{n_new}"), "kernel_us_mean": round(sec * 1e6, 2),
                      "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
@@ -286,7 +287,10 @@ def bench_sample(args, torch, pa, flush_caches, stream):
                     "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "spec_sample_chunks + spec_sample_pick",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": (measured_traffic(f"sample:{case.batch}")
+                                 if (k, case.vocab) == (4, W.VOCAB_8B) else None),
+                     "traffic_kernel": "spec_sample_chunks",
                      "kernel_us_mean": round(sec * 1e6, 2), "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:

@@ -97,6 +97,9 @@ typedef struct pa_pool_desc {
     int32_t waves;            /* tuning: waves per workgroup (4 or 8); 0 = automatic */
     int32_t prefetch;         /* tuning: pages held in registers per wave (2..6, at most 4 with
                                  8 waves); 0 = automatic */
+    int32_t prefill_from;     /* query rows per sequence from which a bf16 / fp8 causal call
+                                 runs the chunked-prefill kernel; 0 = automatic (128),
+                                 -1 = never */
 } pa_pool_desc;
 
 typedef struct pa_pool pa_pool;
@@ -110,6 +113,9 @@ typedef struct pa_plan {
     int32_t waves;            /* waves per workgroup */
     int32_t grid;             /* workgroups of the partition kernel */
     int32_t reduce;           /* 1 if the split-K reduce kernel runs */
+    int32_t kernel;           /* 0: partition kernel (+ reduce); 1: chunked-prefill kernel
+                                 (256 rows of one sequence and kv head per workgroup, no
+                                 split, no workspace) */
 } pa_plan;
 
 /* Bytes of the K and V pool arrays for a pool of this shape (host only). */

@@ -44,13 +44,14 @@ class pa_pool_desc(ctypes.Structure):
         ("partition_pages", ctypes.c_int32),
         ("waves", ctypes.c_int32),
         ("prefetch", ctypes.c_int32),
+        ("prefill_from", ctypes.c_int32),
     ]
 
 
 class pa_plan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("partition_pages", "num_splits", "row_tiles", "row_chunks", "waves", "grid",
-                 "reduce")]
+                 "reduce", "kernel")]
 
 
 def _load():
@@ -175,7 +176,8 @@ def paged_attn_pool_bytes(num_pages: int, num_kv_heads: int, kv_dtype: int,
 
 
 def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None,
-                           partition_pages: int = 0, waves: int = 0, prefetch: int = 0) -> Pool:
+                           partition_pages: int = 0, waves: int = 0, prefetch: int = 0,
+                           prefill_from: int = 0) -> Pool:
     """v: [num_pages][Hkv][16][128]; k: the same elements in the chunked K layout
     [num_pages][Hkv][128/x][16][x], x = 16 bytes / element size (device tensors of
     float32, bfloat16 or fp8 bytes)."""
@@ -184,7 +186,8 @@ def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_sca
     desc = pa_pool_desc(num_pages=v.shape[0], page_size=v.shape[2], num_kv_heads=v.shape[1],
                         head_dim=v.shape[3], kv_dtype=_kv_code(k), k=_dptr(k), v=_dptr(v),
                         k_scale=_dptr(k_scale), v_scale=_dptr(v_scale),
-                        partition_pages=partition_pages, waves=waves, prefetch=prefetch)
+                        partition_pages=partition_pages, waves=waves, prefetch=prefetch,
+                        prefill_from=prefill_from)
     h = ctypes.c_void_p()
     _check(_lib.paged_attn_create_pool(ctypes.byref(desc), ctypes.byref(h)),
            "paged_attn_create_pool")

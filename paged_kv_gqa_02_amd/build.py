@@ -2,35 +2,58 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "spec_sample.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "prefill.hip", "spec_sample.hip")]
 LIB = os.path.join(PKG, "libpaged_attn.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden", "-Wall",
     # no packed fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# The prefill kernel never feeds a NaN to a min / max (dead keys are masked by
+# index before the row max, dead V rows zeroed), so its max reductions need no
+# NaN quieting: relaxed NaN handling and the non-IEEE mode drop those moves.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"]}
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in res.stderr.splitlines() if noise not in x)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (each with its own flags), then link."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmpdir = tempfile.mkdtemp(prefix="paged_attn_build_")
+    try:
+        objs, notes = [], []
+        for src in SRCS:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            extra = FILE_FLAGS.get(os.path.basename(src), [])
+            notes.append(_run([hipcc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-c", src, "-o", obj]))
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        notes.append(_run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
+    if verbose:
+        for n in notes:
+            if n.strip():
+                print(n, file=sys.stderr)
     return LIB
 
 

@@ -41,12 +41,16 @@
 #include <string>
 #include <vector>
 
+#include "cdna4.h"
 #include "paged_attn.h"
+#include "prefill.h"
 #include "status.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
 namespace {
+
+using namespace cdna4;
 
 constexpr int kPage = 16;
 constexpr int kHeadDim = 128;
@@ -63,13 +67,6 @@ constexpr int kAccStride = kHeadDim + 4;    // LDS row stride of the wave merge 
 // than this many log2 units, so weights stay <= 2^8 (safe in fp32 and bf16)
 // and the accumulator is rescaled on few pages.
 constexpr float kRescaleSlack = 8.0f;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -98,67 +95,6 @@ struct Args {
     int32_t part_pages;
     float scale_log2;      // scale * log2(e)
 };
-
-// ---------------------------------------------------------------------------
-// small helpers
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t bf16_bits(float x)
-{
-    return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-
-__device__ __forceinline__ float bf16_float(uint32_t bits16)
-{
-    return __uint_as_float(bits16 << 16);
-}
-
-__device__ __forceinline__ float fast_exp2(float x)
-{
-    return __builtin_amdgcn_exp2f(x);
-}
-
-// Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32,
-// l^48) with the gfx950 lane-swap instructions: swapping a register with
-// itself leaves one copy of each partner value in the returned pair.
-__device__ __forceinline__ float group_max(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const uint32_t w = __float_as_uint(y);
-    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float group_sum(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const uint32_t w = __float_as_uint(y);
-    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Two E4M3 bytes (low or high half of w) -> two bf16 in one dword.  E4M3 is
-// a subset of bf16, so the conversion is exact.
-template <bool kHigh>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
-{
-    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// 8 E4M3 bytes -> 8 bf16
-__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
-{
-    u32x4 r;
-    r[0] = fp8x2_to_bf16x2<false>(w0);
-    r[1] = fp8x2_to_bf16x2<true>(w0);
-    r[2] = fp8x2_to_bf16x2<false>(w1);
-    r[3] = fp8x2_to_bf16x2<true>(w1);
-    return r;
-}
 
 // ---------------------------------------------------------------------------
 // one page of K and V for one kv head, in MFMA operand layout
@@ -356,17 +292,7 @@ struct VOps {
     float vs;       // V scale folded into the probabilities (1 for bf16)
 };
 
-__device__ __forceinline__ void transpose_v(VOps& o, const u32x4 (&v)[4])
-{
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const int w = db >> 1;
-        const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
-        o.a[db] = __builtin_bit_cast(i16x4, u32x2{lo, hi});
-    }
-}
+__device__ __forceinline__ void transpose_v(VOps& o, const u32x4 (&v)[4]) { v_operands(o.a, v); }
 
 __device__ __forceinline__ void prepare_v(VOps& o, const Page<KV_BF16>& pg)
 {
@@ -941,6 +867,8 @@ int cu_count()
 // pages when the query tile (two row tiles, or fp8 conversion) needs the
 // registers.
 constexpr int kWaves = 4;
+// query rows per sequence from which bf16 / fp8 causal calls take the chunked-prefill kernel
+constexpr int kPrefillFromRows = 128;
 constexpr int default_prefetch(pa_dtype kv, int row_tiles)
 {
     return (row_tiles == 1 && kv != PA_FP8_E4M3) ? 3 : 2;
@@ -962,7 +890,7 @@ struct pa_pool {
 namespace {
 
 pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, int32_t max_len,
-                    pa_plan* pl)
+                    pa_plan* pl, bool allow_prefill = true)
 {
     if (!pool || !pl) return fail(PA_ERR_INVALID_ARG, "null pool or plan");
     const pa_pool_desc& d = pool->d;
@@ -973,6 +901,23 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     if (max_len < n) return fail(PA_ERR_INVALID_ARG, "max_seq_len < q_per_seq");
     const int64_t rows = (int64_t)(hq / d.num_kv_heads) * n;
     if (rows > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many query rows");
+    // chunked prefill: many rows per sequence make the call a dense contraction
+    const int prefill_from = d.prefill_from == 0 ? kPrefillFromRows : d.prefill_from;
+    if (allow_prefill && d.kv_dtype != PA_F32 && prefill_from > 0 && n >= prefill_from &&
+        (max_len + kPage - 1) / kPage <= kPrefillMaxPages) {
+        const int64_t row_blocks = (rows + kPrefillRows - 1) / kPrefillRows;
+        const int64_t grid = (int64_t)batch * d.num_kv_heads * row_blocks;
+        if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+        pl->partition_pages = (max_len + kPage - 1) / kPage;
+        pl->num_splits = 1;
+        pl->row_tiles = kPrefillRows / 16;
+        pl->row_chunks = (int32_t)row_blocks;
+        pl->waves = 4;
+        pl->grid = (int32_t)grid;
+        pl->reduce = 0;
+        pl->kernel = 1;
+        return PA_OK;
+    }
     const int nt = (int)std::min<int64_t>(kMaxRowTiles, (rows + 15) / 16);
     const int64_t row_chunks = (rows + 16 * nt - 1) / (16 * nt);
     const int max_pages = (max_len + kPage - 1) / kPage;
@@ -1003,6 +948,7 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     pl->waves = waves;
     pl->grid = (int32_t)grid;
     pl->reduce = ns > 1 ? 1 : 0;
+    pl->kernel = 0;
     return PA_OK;
 }
 
@@ -1080,7 +1026,9 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
         return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_pages_per_seq");
     if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     pa_plan pl;
-    pa_status stt = make_plan(pool, batch, n, hq, max_seq_len, &pl);
+    // the chunked-prefill kernel writes O in 16-byte pieces
+    const bool out16 = reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    pa_status stt = make_plan(pool, batch, n, hq, max_seq_len, &pl, out16);
     if (stt != PA_OK) return stt;
     const size_t need = workspace_for(pl, batch, n, hq);
     if (need > 0) {
@@ -1126,8 +1074,37 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (pl.kernel == 1 && tree_mask)
+        return fail(PA_ERR_UNSUPPORTED, "draft trees have at most 64 nodes");
     if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), st)) != hipSuccess)
         return hip_fail(e, "hipEventRecord(begin)");
+    if (pl.kernel == 1) {
+        PrefillArgs pa;
+        pa.k = d.k;
+        pa.v = d.v;
+        pa.k_scale = d.k_scale;
+        pa.v_scale = d.v_scale;
+        pa.q = static_cast<const uint16_t*>(q);
+        pa.out = static_cast<uint16_t*>(out);
+        pa.block_table = block_table;
+        pa.seq_lens = seq_lens;
+        pa.page_stride = a.page_stride;
+        pa.num_pages = d.num_pages;
+        pa.max_pages = max_pages_per_seq;
+        pa.batch = batch;
+        pa.n = n;
+        pa.hq = hq;
+        pa.hkv = d.num_kv_heads;
+        pa.group = a.group;
+        pa.rows = a.rows;
+        pa.row_blocks = pl.row_chunks;
+        pa.scale_log2 = a.scale_log2;
+        if ((e = launch_prefill(pa, d.kv_dtype == PA_FP8_E4M3, st)) != hipSuccess)
+            return hip_fail(e, "prefill kernel launch");
+        if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), st)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(end)");
+        return PA_OK;
+    }
     const int pf = d.prefetch > 0 ? d.prefetch : default_prefetch(d.kv_dtype, pl.row_tiles);
     switch (d.kv_dtype) {
     case PA_F32: launch_partition_nt<KV_F32>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
@@ -1188,6 +1165,7 @@ PA_API pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out)
     if (desc->prefetch != 0 && (desc->prefetch < 2 || desc->prefetch > 6 ||
                                 (desc->waves == 8 && desc->prefetch > 4)))
         return fail(PA_ERR_UNSUPPORTED, "prefetch must be 0, 2..6 (2..4 with 8 waves)");
+    if (desc->prefill_from < -1) return fail(PA_ERR_INVALID_ARG, "prefill_from must be >= -1");
     pa_pool* p = new (std::nothrow) pa_pool;
     if (!p) return fail(PA_ERR_INVALID_ARG, "out of host memory");
     p->d = *desc;

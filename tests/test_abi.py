@@ -34,7 +34,7 @@ def test_status_strings():
 def _desc(**kw):
     d = dict(num_pages=64, page_size=16, num_kv_heads=8, head_dim=128, kv_dtype=B.PA_BF16,
              k=FAKE_K, v=FAKE_V, k_scale=None, v_scale=None, partition_pages=0, waves=0,
-             prefetch=0)
+             prefetch=0, prefill_from=0)
     d.update(kw)
     return B.pa_pool_desc(**d)
 
@@ -57,6 +57,7 @@ def _create(**kw):
     (dict(waves=6), B.PA_ERR_UNSUPPORTED),
     (dict(prefetch=9), B.PA_ERR_UNSUPPORTED),
     (dict(waves=8, prefetch=5), B.PA_ERR_UNSUPPORTED),
+    (dict(prefill_from=-2), B.PA_ERR_INVALID_ARG),
 ])
 def test_create_pool_rejects(kw, status):
     st, h = _create(**kw)
@@ -87,6 +88,30 @@ def test_plans_for_named_workloads():
     assert ver.num_splits * ver.partition_pages >= 257
     big = _plan(h, 1, 20, 32, 4096)                  # 80 rows -> two 64-row chunks
     assert big.row_tiles == 4 and big.row_chunks == 2
+    assert one.kernel == ver.kernel == big.kernel == 0
+    LIB.paged_attn_destroy_pool(h)
+
+
+def test_prefill_plans():
+    st, h = _create(num_pages=8192)
+    pre = _plan(h, 4, 512, 32, 2048)                 # 2048 rows -> 8 blocks of 256, no split
+    assert pre.kernel == 1 and pre.row_chunks == 8 and pre.grid == 4 * 8 * 8
+    assert pre.reduce == 0 and pre.num_splits == 1
+    assert _plan(h, 4, 127, 32, 2048).kernel == 0    # below 128 rows per sequence
+    assert _plan(h, 1, 130, 32, 2048).row_chunks == 3    # 520 rows: the last block partial
+    assert _plan(h, 1, 128, 32, 2048 * 16 + 16).kernel == 0   # past the page-id table
+    ws = ctypes.c_size_t(1)
+    assert LIB.paged_attn_workspace_bytes(h, 4, 512, 32, 2048, ctypes.byref(ws)) == 0
+    assert ws.value == 0
+    LIB.paged_attn_destroy_pool(h)
+    st, h = _create(num_pages=8192, prefill_from=-1)  # never
+    assert _plan(h, 4, 512, 32, 2048).kernel == 0
+    LIB.paged_attn_destroy_pool(h)
+    st, h = _create(num_pages=8192, prefill_from=16)
+    assert _plan(h, 4, 16, 32, 2048).kernel == 1
+    LIB.paged_attn_destroy_pool(h)
+    st, h = _create(num_pages=8192, kv_dtype=B.PA_F32)   # fp32 stays on the partition kernel
+    assert _plan(h, 4, 512, 32, 2048).kernel == 0
     LIB.paged_attn_destroy_pool(h)
 
 

@@ -1,6 +1,8 @@
 """Chunked-prefill attention over the paged cache: hundreds of query rows per
 sequence, each attending to the earlier chunks' keys and causally within its
-own chunk.  Checked against the oracle, and (at the full workload) against the
+own chunk.  Every case runs through the chunked-prefill kernel (the automatic
+choice from 128 rows per sequence) and through the partition kernel
+(prefill_from = -1), against the oracle; at the full workload also against the
 pin that prefill row i is the decode of the same query at length L - n + i + 1.
 """
 import numpy as np
@@ -9,9 +11,11 @@ import torch
 
 import workloads as W
 from workloads.device import to_device, to_numpy_f64
-from test_gpu_parity import MAX_ABS, check, run_gpu, run_oracle, say, small_case
+from test_gpu_parity import MAX_ABS, check, run_oracle, say, small_case
 
 pytestmark = pytest.mark.gpu
+
+KERNELS = {"prefill": 0, "partition": -1}      # pool prefill_from
 
 
 @pytest.fixture(scope="module")
@@ -22,32 +26,81 @@ def pa():
     return lib
 
 
+def run(pa, case, kernel, dev=None):
+    d = dev if dev is not None else to_device(case)
+    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale,
+                                     prefill_from=KERNELS[kernel])
+    plan = pa.paged_attn_plan(pool, case.batch, case.q_per_seq, case.num_q_heads,
+                              case.max_seq_len)
+    say(f"[gpu prefill] {case.name} kernel={kernel} (plan {plan['kernel']}) kv={case.kv_dtype} "
+        f"B={case.batch} n={case.q_per_seq} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"lens={list(case.seq_lens)} seed={case.seed}")
+    want = 1 if kernel == "prefill" and case.kv_dtype != "f32" else 0
+    assert plan["kernel"] == want
+    out = torch.empty_like(d.q)
+    ws = pa.workspace_for(pool, d.q, case.max_seq_len)
+    pa.paged_attn_verify(pool, d.q, out, d.block_table, d.seq_lens, case.max_seq_len,
+                         case.scale, ws)
+    torch.cuda.synchronize()
+    return to_numpy_f64(out)
+
+
+@pytest.mark.parametrize("kernel", ["prefill", "partition"])
 @pytest.mark.parametrize("kv,heads", [("bf16", (32, 8)), ("f32", (8, 2)), ("fp8", (16, 2))])
-def test_prefill_chunk_matches_oracle(pa, kv, heads):
+def test_prefill_chunk_matches_oracle(pa, kernel, kv, heads):
     # a first chunk (no context), a chunk after a ragged context, a chunk ending mid-page
     n = 256
     case = small_case(kv, n, heads[0], heads[1], [n, n + 300, n + 17 + 16 * 20], seed=900)
-    check(run_gpu(pa, case), run_oracle(case), kv, f"prefill n={n} {kv}")
+    check(run(pa, case, kernel), run_oracle(case), kv, f"prefill n={n} {kv} {kernel}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("n,heads,lens", [
+    (130, (32, 8), [130, 131, 400, 1000]),      # 520 rows: a partial last block of 8
+    (128, (64, 8), [128, 129 + 16 * 7, 600]),   # G = 8 (1024 rows)
+    (200, (8, 8), [200, 215, 777]),             # G = 1 (MHA): 200 rows, one partial block
+    (160, (4, 1), [160, 161, 2000]),            # MQA, an odd page count, a long context
+])
+def test_prefill_kernel_edge_shapes(pa, kv, n, heads, lens):
+    case = small_case(kv, n, heads[0], heads[1], lens, seed=910 + n)
+    check(run(pa, case, "prefill"), run_oracle(case), kv, f"prefill edge n={n} {heads} {kv}")
 
 
 def test_prefill_workload_structure_in_fp32(pa):
-    """Same shape in fp32 (1e-5 gate): the first chunk, fully causal."""
+    """Same shape in fp32 (1e-5 gate; the partition kernel): the first chunk, fully causal."""
     case = W.workload("prefill", kv_dtype="f32", q_dtype="f32")
-    gpu = run_gpu(pa, case, label="fp32 structure")
+    gpu = run(pa, case, "partition")
     check(gpu[3:4], run_oracle(case, seqs=[3]), "f32", "prefill fp32 seq 3")
 
 
-def test_prefill_workload_native(pa):
+@pytest.mark.parametrize("kernel", ["prefill", "partition"])
+def test_prefill_workload_native(pa, kernel):
     case = W.workload("prefill")
-    gpu = run_gpu(pa, case, label="native")
-    check(gpu[3:4], run_oracle(case, seqs=[3]), "bf16", "prefill bf16 seq 3")
+    gpu = run(pa, case, kernel)
+    check(gpu[3:4], run_oracle(case, seqs=[3]), "bf16", f"prefill bf16 seq 3 {kernel}")
+
+
+def test_prefill_kernels_agree_at_the_workload(pa):
+    case = W.workload("prefill")
+    d = to_device(case)
+    a, b = run(pa, case, "prefill", dev=d), run(pa, case, "partition", dev=d)
+    err = float(np.abs(a - b).max())
+    say(f"    prefill vs partition kernel: max_abs={err:.3e}")
+    assert err <= MAX_ABS["bf16"]
+
+
+def test_prefill_kernel_is_deterministic(pa):
+    case = W.workload("prefill")
+    d = to_device(case)
+    a, b = run(pa, case, "prefill", dev=d), run(pa, case, "prefill", dev=d)
+    assert np.array_equal(a, b)
 
 
 def test_prefill_rows_are_stacked_decodes(pa):
     """Row i of a chunk equals the decode of its query over the first L - n + i + 1 keys."""
     case = W.workload("prefill")
     d = to_device(case)
-    full = run_gpu(pa, case, dev=d, label="rows vs decode")
+    full = run(pa, case, "prefill", dev=d)
     pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale)
     n = case.q_per_seq
     rows = [0, 1, 15, 16, 255, 383, n - 2, n - 1]

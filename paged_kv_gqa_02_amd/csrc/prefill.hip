@@ -21,7 +21,10 @@
 //    register holds data in flight.  Pages keep the pool's layouts: a wave's
 //    K operand is one contiguous KiB per LDS read, a V operand four 256-byte
 //    rows.  E4M3 pages are converted to bf16 (exactly) as operands are read,
-//    their scales applied to the scores and probabilities;
+//    their scales applied to the scores and probabilities.  bf16 V operands
+//    come straight from LDS with gfx950's transposing read (ds_read_b64_tr_b16),
+//    V rows being stored with a 16-byte-chunk XOR swizzle (chosen per lane in
+//    the direct copy) so that those reads are free of bank conflicts;
 //  * QK^T is v_mfma_f32_16x16x32_bf16 per page (tokens as M, rows as N); PV is
 //    the same instruction over the 32 tokens of the pair: the K index of the
 //    MFMA is free to enumerate tokens in any order, so the two pages' QK
@@ -90,9 +93,15 @@ __device__ __forceinline__ void wait_dma()
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// bf16 V rows in LDS: 16-byte chunk c of row r is stored at chunk c ^ vswz(r),
+// so that the eight rows one transposing read touches fall in distinct banks.
+__device__ __forceinline__ int vswz(int row) { return 2 * (row & 7); }
+
 // Pair j into its stage, 1 KiB per wave instruction: piece p of the stage is
 // slab p / (pieces per slab) (K page 0, K page 1, V page 0, V page 1) at
 // offset 1 KiB * (p % pieces per slab); wave w copies pieces w * n .. w * n + n - 1.
+// A bf16 V piece holds rows 4i .. 4i + 3; lane l lands at row 4i + l / 16,
+// chunk l % 16, and fetches the chunk that the swizzle puts there.
 template <bool FP8>
 __device__ __forceinline__ void issue_pair(const PrefillArgs& a, const int32_t* ids, int npairs,
                                            int j, int kh, int wave, int lane, uint32_t stage_lds)
@@ -109,7 +118,12 @@ __device__ __forceinline__ void issue_pair(const PrefillArgs& a, const int32_t* 
         const uint8_t* src = static_cast<const uint8_t*>(slab < 2 ? a.k : a.v) +
                              ((int64_t)page * a.page_stride + (int64_t)kh * kSlab) * Ly::kElem +
                              1024 * (piece % kPieces);
-        dma16(src, 16 * lane, __builtin_amdgcn_readfirstlane(stage_lds + 1024 * piece));
+        uint32_t voff = 16 * lane;
+        if (!FP8 && slab >= 2) {
+            const int row = 4 * (piece % kPieces) + (lane >> 4);
+            voff = 256 * (lane >> 4) + 16 * ((lane & 15) ^ vswz(row));
+        }
+        dma16(src, voff, __builtin_amdgcn_readfirstlane(stage_lds + 1024 * piece));
     }
 }
 
@@ -263,18 +277,29 @@ __global__ __launch_bounds__(kThreads) void paged_attn_prefill(PrefillArgs a)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint8_t* vp = st + (2 + h) * Ly::kPageBytes;
-                u32x4 vr[4];
+                if constexpr (FP8) {
+                    // a[db] = {V[4g + s][8 l16 + db], s = 0..3}: rows read, then permuted
+                    u32x4 vr[4];
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int row = 4 * g + s4;
-                    if constexpr (FP8) {
-                        const u32x2 w = *reinterpret_cast<const u32x2*>(vp + row * kHeadDim + 8 * l16);
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(vp + (4 * g + s4) * kHeadDim + 8 * l16);
                         vr[s4] = fp8x8_to_bf16x8(w[0], w[1]);
-                    } else {
-                        vr[s4] = *reinterpret_cast<const u32x4*>(vp + row * 2 * kHeadDim + 16 * l16);
+                    }
+                    v_operands(av[h], vr);
+                } else {
+                    // a[db] = {V[4g + k][16 db + l16], k = 0..3} from one transposing
+                    // read: in each 16-lane group, lane j names 4 elements of row
+                    // 4g + j / 4 at dims 16 db + 4 (j % 4), and lane i receives the
+                    // i % 4-th element of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4
+                    const int row = 4 * g + (l16 >> 2);
+                    const uint8_t* rp = vp + 2 * kHeadDim * row + 8 * (l16 & 1);
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) {
+                        const int chunk = 2 * db + ((l16 & 3) >> 1);
+                        av[h][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(rp + 16 * (chunk ^ vswz(row))));
                     }
                 }
-                v_operands(av[h], vr);
             }
 #pragma unroll
             for (int db = 0; db < 8; ++db)
@@ -345,7 +370,8 @@ __global__ __launch_bounds__(kThreads) void paged_attn_prefill(PrefillArgs a)
     // no copy may still be writing this workgroup's LDS when it exits
     wait_dma<0>();
 
-    // epilogue: lane holds O[row l16][32 g + 8 v + db] of each tile
+    // epilogue: lane holds O[row l16][32 g + 8 v + db] (E4M3 pools) or
+    // O[row l16][16 db + 4 g + v] (bf16 pools) of each tile
 #pragma unroll
     for (int tt = 0; tt < kTiles; ++tt) {
         const int r = wrow0 + tt * 16 + l16;
@@ -353,15 +379,25 @@ __global__ __launch_bounds__(kThreads) void paged_attn_prefill(PrefillArgs a)
         if (r < a.rows) {
             const int i = r / a.group;
             const int h = kh * a.group + (r - i * a.group);
-            uint16_t* orow = a.out + (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim + 32 * g;
+            uint16_t* orow = a.out + (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim;
+            if constexpr (FP8) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                uint32_t w[4];
+                for (int v = 0; v < 4; ++v) {
+                    uint32_t w[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = bf16_bits(acc[tt][2 * e][v] * inv) |
-                           (bf16_bits(acc[tt][2 * e + 1][v] * inv) << 16);
-                *reinterpret_cast<u32x4*>(orow + 8 * v) = u32x4{w[0], w[1], w[2], w[3]};
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = bf16_bits(acc[tt][2 * e][v] * inv) |
+                               (bf16_bits(acc[tt][2 * e + 1][v] * inv) << 16);
+                    *reinterpret_cast<u32x4*>(orow + 32 * g + 8 * v) = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            } else {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const f32x4 x = acc[tt][db] * inv;
+                    *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) =
+                        u32x2{bf16_bits(x[0]) | (bf16_bits(x[1]) << 16),
+                              bf16_bits(x[2]) | (bf16_bits(x[3]) << 16)};
+                }
             }
         }
     }

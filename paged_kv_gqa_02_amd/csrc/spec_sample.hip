@@ -15,9 +15,10 @@
 // K scalar lookups.  Two kernels:
 //  * pass 1, one wave per (4096-entry chunk of the row, sequence): finds the
 //    first rejection (one lane per draft, a wave ballot); each lane loads 64
-//    consecutive entries straight into registers (16-byte non-temporal loads,
-//    all in flight at once) and the wave writes the chunk's sums of the
-//    sampling weights and of p, in binary64;
+//    consecutive entries straight into registers (16-byte loads, all in flight
+//    at once; plain rather than non-temporal, so that the wave's 16-byte
+//    pieces of one cache line meet in L1) and the wave writes the chunk's sums
+//    of the sampling weights and of p, in binary64;
 //  * pass 2, one wave per sequence: folds the chunk sums, finds the chunk in
 //    which the running sum first exceeds u * total, re-reads that chunk only
 //    and finds the token inside it.

@@ -405,7 +405,7 @@ def main():
     else:
         kern_ms = call_ms
     log(f"timed {args.steps} steps: call {call_ms.mean() * 1e3:.1f} us, "
-        f"partition kernel {kern_ms.mean() * 1e3:.1f} us")
+        f"attention kernel {kern_ms.mean() * 1e3:.1f} us")
 
     nbytes = case.algorithmic_bytes()
     flops = attention_flops(case)
@@ -441,7 +441,8 @@ def main():
                     "p50": round(float(np.percentile(call_ms, 50)) * 1e3, 2),
                     "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
         "plan": plan,
-        "roofline": {"bound": "hbm", "kernel": "paged_attn_partition",
+        "roofline": {"bound": "hbm",
+                     "kernel": "paged_attn_prefill" if plan.get("kernel") == 1 else "paged_attn_partition",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(case.name),

@@ -109,10 +109,11 @@ def test_append_then_attention(pa, kv):
 
 
 @pytest.mark.parametrize("name,n_new,src", [("decode8b", 1, "bf16"), ("verify", 5, "bf16"),
-                                            ("fp8long", 1, "f32")])
+                                            ("fp8long", 1, "f32"), ("decode8b", 256, "bf16"),
+                                            ("fp8long", 256, "bf16")])
 def test_append_workloads(pa, name, n_new, src):
     case = W.workload(name)
-    kn, vn = W.append_inputs(case, n_new, src, 430)
+    kn, vn = W.append_inputs(case, n_new, src, 20261202)     # the inputs bench.py --op append times
     assert_pools_equal(gpu_append(pa, case, kn, vn, n_new),
                        oracle_append(case, kn, vn, src, n_new))
 

@@ -83,6 +83,13 @@ def test_matches_oracle_at_8b_vocab(pa, seed):
     assert ties == 0
 
 
+@pytest.mark.parametrize("batch", [64, 8])
+def test_matches_oracle_at_the_bench_configurations(pa, batch):
+    """The inputs bench.py --op sample times (same generator and seed)."""
+    c = W.sampler_inputs(batch, 4, W.VOCAB_8B, 20261202)
+    check(c, gpu_sample(pa, c), oracle.rejection_sample(c.p, c.q, c.draft, c.u_accept, c.u_sample))
+
+
 @pytest.mark.parametrize("B,K,V", [(1, 0, 1), (3, 1, 7), (5, 4, 4095), (5, 4, 4096), (5, 4, 4097),
                                    (7, 3, 8193), (4, 64, 300), (9, 0, 50000), (2, 7, 1 << 20)])
 def test_matches_oracle_at_edge_shapes(pa, B, K, V):

@@ -306,13 +306,15 @@ __global__ __launch_bounds__(kThreads) void paged_attn_prefill(PrefillArgs a)
                 va[db] = __builtin_bit_cast(
                     bf16x8, __builtin_shufflevector(av[0][db], av[1][db], 0, 1, 2, 3, 4, 5, 6, 7));
         }
+        // Phase 1, every tile: raw scores.  The scale (and an E4M3 page's K
+        // scale) is folded into the exponent: p = exp2(s * f - m) with f > 0,
+        // so max(s * f) = f * max(s).
+        float f[2];
 #pragma unroll
-        for (int tt = 0; tt < kTiles; ++tt) {
-            // raw scores; the scale (and an E4M3 page's K scale) is folded into
-            // the exponent: p = exp2(s * f - m), f > 0, so max(s * f) = f * max(s)
-            float sc[8];
-            float f[2];
-            float mx = -INFINITY;
+        for (int h = 0; h < 2; ++h) f[h] = FP8 ? a.scale_log2 * ks[h] : a.scale_log2;
+        float sc[kTiles][8];
+#pragma unroll
+        for (int tt = 0; tt < kTiles; ++tt)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
@@ -320,26 +322,38 @@ __global__ __launch_bounds__(kThreads) void paged_attn_prefill(PrefillArgs a)
                 for (int c = 0; c < 4; ++c)
                     s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[h][c]),
                                                                  qf[tt][c], s4, 0, 0, 0);
-                f[h] = FP8 ? a.scale_log2 * ks[h] : a.scale_log2;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sc[4 * h + v] = s4[v];
+                for (int v = 0; v < 4; ++v) sc[tt][4 * h + v] = s4[v];
             }
-            if (need_mask) {
+        if (need_mask) {
+#pragma unroll
+            for (int tt = 0; tt < kTiles; ++tt)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int tok = base + 16 * (e >> 2) + 4 * g + (e & 3);
-                    sc[e] = tok <= lim[tt] ? sc[e] : -INFINITY;
+                    sc[tt][e] = tok <= lim[tt] ? sc[tt][e] : -INFINITY;
                 }
-            }
+        }
+        // Phase 2: row maxima, and one rescale branch for all tiles (a tile
+        // whose maximum did not move is multiplied by exp2(0) = 1, exactly)
+        float mx[kTiles];
+        bool grow_any = false;
+#pragma unroll
+        for (int tt = 0; tt < kTiles; ++tt) {
+            float x = -INFINITY;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const float ph = fmaxf(fmaxf(sc[4 * h], sc[4 * h + 1]), fmaxf(sc[4 * h + 2], sc[4 * h + 3]));
-                mx = fmaxf(mx, ph * f[h]);
+                const float ph = fmaxf(fmaxf(sc[tt][4 * h], sc[tt][4 * h + 1]),
+                                       fmaxf(sc[tt][4 * h + 2], sc[tt][4 * h + 3]));
+                x = fmaxf(x, ph * f[h]);
             }
-            mx = group_max(mx);
-            const bool grow = mx > m[tt] + kRescaleSlack;
-            if (__any(grow)) {
-                const float mnew = grow ? mx : m[tt];
+            mx[tt] = group_max(x);
+            grow_any |= mx[tt] > m[tt] + kRescaleSlack;
+        }
+        if (__any(grow_any)) {
+#pragma unroll
+            for (int tt = 0; tt < kTiles; ++tt) {
+                const float mnew = mx[tt] > m[tt] + kRescaleSlack ? mx[tt] : m[tt];
                 const float alpha = fast_exp2(m[tt] - mnew);
                 m[tt] = mnew;
                 l[tt] *= alpha;
@@ -347,11 +361,16 @@ __global__ __launch_bounds__(kThreads) void paged_attn_prefill(PrefillArgs a)
 #pragma unroll
                 for (int db = 0; db < 8; ++db) acc[tt][db] *= alpha;
             }
+        }
+        // Phase 3, one basic block: weights and PV of every tile, so that one
+        // tile's exponentials can issue while the other's MFMAs run
+#pragma unroll
+        for (int tt = 0; tt < kTiles; ++tt) {
             uint32_t pb[8];
             float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = fast_exp2(__builtin_fmaf(sc[e], f[e >> 2], -m[tt]));
+                const float p = fast_exp2(__builtin_fmaf(sc[tt][e], f[e >> 2], -m[tt]));
                 pb[e] = bf16_bits(FP8 ? p * vs[e >> 2] : p);
                 if constexpr (FP8) psum += p;
             }

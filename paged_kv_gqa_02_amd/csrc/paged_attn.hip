@@ -610,19 +610,29 @@ __global__ __launch_bounds__(kReduceThreads) void paged_attn_reduce(Args a)
     __shared__ float sm_l[kMaxSplits];
     const int64_t orow = blockIdx.x;                 // (b * n + i) * hq + h
     const int b = (int)(orow / ((int64_t)a.n * a.hq));
+    const int t = threadIdx.x;
+    // The partials and (max, sum) pairs of the plan's splits are requested
+    // together with the sequence length, before the number this sequence
+    // actually wrote is known (entries past it are read but never used), so
+    // the merge waits for one memory round trip instead of two.
+    const float* src = a.part_acc + orow * a.num_splits * kHeadDim + t;
+    float x[kReduceInFlight];
+#pragma unroll
+    for (int sp = 0; sp < kReduceInFlight; ++sp)
+        x[sp] = src[min(sp, a.num_splits - 1) * kHeadDim];
+    float mt = 0.f, lt = 0.f;
+    if (t < a.num_splits) {
+        const float* ml = a.part_ml + (orow * a.num_splits + t) * 2;
+        mt = ml[0];
+        lt = ml[1];
+    }
     const int L = min(a.seq_lens[b], a.max_pages * kPage);
     const int npages = (L + kPage - 1) / kPage;
     const int ns = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
     if (ns <= 1) return;                             // written by the partition kernel
-    const int t = threadIdx.x;
-    const float* src = a.part_acc + orow * a.num_splits * kHeadDim + t;
-    float x[kReduceInFlight];
-#pragma unroll
-    for (int sp = 0; sp < kReduceInFlight; ++sp) x[sp] = sp < ns ? src[sp * kHeadDim] : 0.f;
     if (t < ns) {
-        const float* ml = a.part_ml + (orow * a.num_splits + t) * 2;
-        sm_m[t] = ml[0];
-        sm_l[t] = ml[1];
+        sm_m[t] = mt;
+        sm_l[t] = lt;
     }
     __syncthreads();
     float mm = kNoMax;

@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode8b", choices=W.WORKLOADS)
     ap.add_argument("--partition-pages", type=int, default=0)
+    ap.add_argument("--staged-from", type=int, default=0,
+                    help="pool knob: rows per sequence from which causal calls take the "
+                         "LDS-staged kernel (0 = library default, -1 = never)")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
@@ -355,7 +358,7 @@ def main():
     case = W.workload(args.workload)
     dev = to_device(case)
     pool = pa.paged_attn_create_pool(dev.k, dev.v, dev.k_scale, dev.v_scale,
-                                     args.partition_pages)
+                                     args.partition_pages, staged_from=args.staged_from)
     plan = pa.paged_attn_plan(pool, case.batch, case.q_per_seq, case.num_q_heads,
                               case.max_seq_len)
     out = torch.empty_like(dev.q)
@@ -407,6 +410,10 @@ def main():
     log(f"timed {args.steps} steps: call {call_ms.mean() * 1e3:.1f} us, "
         f"attention kernel {kern_ms.mean() * 1e3:.1f} us")
 
+    # chunked prefill, and draft trees on bf16 / fp8 pools, run the LDS-staged kernel
+    staged = plan.get("kernel") == 1 or (case.tree_mask is not None and case.kv_dtype != "f32"
+                                         and args.staged_from != -1)
+    kernel_name = "paged_attn_staged" if staged else "paged_attn_partition"
     nbytes = case.algorithmic_bytes()
     flops = attention_flops(case)
     call_s = float(call_ms.mean()) / 1e3
@@ -442,7 +449,7 @@ def main():
                     "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
         "plan": plan,
         "roofline": {"bound": "hbm",
-                     "kernel": "paged_attn_prefill" if plan.get("kernel") == 1 else "paged_attn_partition",
+                     "kernel": kernel_name,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(case.name),

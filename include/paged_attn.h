@@ -97,9 +97,11 @@ typedef struct pa_pool_desc {
     int32_t waves;            /* tuning: waves per workgroup (4 or 8); 0 = automatic */
     int32_t prefetch;         /* tuning: pages held in registers per wave (2..6, at most 4 with
                                  8 waves); 0 = automatic */
-    int32_t prefill_from;     /* query rows per sequence from which a bf16 / fp8 causal call
-                                 runs the chunked-prefill kernel; 0 = automatic (128),
-                                 -1 = never */
+    int32_t staged_from;      /* the LDS-staged kernel (pages staged once per workgroup and
+                                 shared by its waves): a bf16 / fp8 causal call with at
+                                 least this many query rows per sequence takes it
+                                 (0 = automatic: 128), and so does every bf16 / fp8 draft-
+                                 tree call; -1 = never */
 } pa_pool_desc;
 
 typedef struct pa_pool pa_pool;
@@ -113,9 +115,11 @@ typedef struct pa_plan {
     int32_t waves;            /* waves per workgroup */
     int32_t grid;             /* workgroups of the partition kernel */
     int32_t reduce;           /* 1 if the split-K reduce kernel runs */
-    int32_t kernel;           /* 0: partition kernel (+ reduce); 1: chunked-prefill kernel
-                                 (256 rows of one sequence and kv head per workgroup, no
-                                 split, no workspace) */
+    int32_t kernel;           /* 0: partition kernel (+ reduce); 1: LDS-staged kernel for
+                                 chunked prefill (256 rows of one sequence and kv head per
+                                 workgroup, no split, no workspace).  Draft-tree calls on
+                                 bf16 / fp8 pools run the LDS-staged kernel with 64 rows per
+                                 workgroup under the split plan reported here. */
 } pa_plan;
 
 /* Bytes of the K and V pool arrays for a pool of this shape (host only). */

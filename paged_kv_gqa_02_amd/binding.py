@@ -44,7 +44,7 @@ class pa_pool_desc(ctypes.Structure):
         ("partition_pages", ctypes.c_int32),
         ("waves", ctypes.c_int32),
         ("prefetch", ctypes.c_int32),
-        ("prefill_from", ctypes.c_int32),
+        ("staged_from", ctypes.c_int32),
     ]
 
 
@@ -177,7 +177,7 @@ def paged_attn_pool_bytes(num_pages: int, num_kv_heads: int, kv_dtype: int,
 
 def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None,
                            partition_pages: int = 0, waves: int = 0, prefetch: int = 0,
-                           prefill_from: int = 0) -> Pool:
+                           staged_from: int = 0) -> Pool:
     """v: [num_pages][Hkv][16][128]; k: the same elements in the chunked K layout
     [num_pages][Hkv][128/x][16][x], x = 16 bytes / element size (device tensors of
     float32, bfloat16 or fp8 bytes)."""
@@ -187,7 +187,7 @@ def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_sca
                         head_dim=v.shape[3], kv_dtype=_kv_code(k), k=_dptr(k), v=_dptr(v),
                         k_scale=_dptr(k_scale), v_scale=_dptr(v_scale),
                         partition_pages=partition_pages, waves=waves, prefetch=prefetch,
-                        prefill_from=prefill_from)
+                        staged_from=staged_from)
     h = ctypes.c_void_p()
     _check(_lib.paged_attn_create_pool(ctypes.byref(desc), ctypes.byref(h)),
            "paged_attn_create_pool")

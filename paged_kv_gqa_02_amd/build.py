@@ -9,7 +9,7 @@ import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "prefill.hip", "spec_sample.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "staged.hip", "spec_sample.hip")]
 LIB = os.path.join(PKG, "libpaged_attn.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -19,10 +19,10 @@ HIPCC_FLAGS = [
     # no packed fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# The prefill kernel never feeds a NaN to a min / max (dead keys are masked by
-# index before the row max, dead V rows zeroed), so its max reductions need no
-# NaN quieting: relaxed NaN handling and the non-IEEE mode drop those moves.
-FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"]}
+# The LDS-staged kernel never feeds a NaN to a min / max (dead keys are masked
+# by index before the row max, dead V rows zeroed), so its max reductions need
+# no NaN quieting: relaxed NaN handling and the non-IEEE mode drop those moves.
+FILE_FLAGS = {"staged.hip": ["-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"]}
 
 
 def _run(cmd):

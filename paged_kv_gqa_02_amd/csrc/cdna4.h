@@ -23,6 +23,15 @@ __device__ __forceinline__ uint32_t bf16_bits(float x)
     return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// two floats to bf16 (round to nearest even, as bf16_bits) in one packed
+// conversion: lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi)
+{
+    typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+    typedef float f32v2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32v2){lo, hi}, bf16v2));
+}
+
 __device__ __forceinline__ float bf16_float(uint32_t bits16)
 {
     return __uint_as_float(bits16 << 16);

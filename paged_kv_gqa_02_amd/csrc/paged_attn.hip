@@ -43,7 +43,7 @@
 
 #include "cdna4.h"
 #include "paged_attn.h"
-#include "prefill.h"
+#include "staged.h"
 #include "status.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
@@ -877,8 +877,9 @@ int cu_count()
 // pages when the query tile (two row tiles, or fp8 conversion) needs the
 // registers.
 constexpr int kWaves = 4;
-// query rows per sequence from which bf16 / fp8 causal calls take the chunked-prefill kernel
-constexpr int kPrefillFromRows = 128;
+// query rows per sequence from which bf16 / fp8 causal calls take the LDS-staged
+// (chunked-prefill) kernel
+constexpr int kStagedFromRows = 128;
 constexpr int default_prefetch(pa_dtype kv, int row_tiles)
 {
     return (row_tiles == 1 && kv != PA_FP8_E4M3) ? 3 : 2;
@@ -912,15 +913,15 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     const int64_t rows = (int64_t)(hq / d.num_kv_heads) * n;
     if (rows > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many query rows");
     // chunked prefill: many rows per sequence make the call a dense contraction
-    const int prefill_from = d.prefill_from == 0 ? kPrefillFromRows : d.prefill_from;
-    if (allow_prefill && d.kv_dtype != PA_F32 && prefill_from > 0 && n >= prefill_from &&
-        (max_len + kPage - 1) / kPage <= kPrefillMaxPages) {
-        const int64_t row_blocks = (rows + kPrefillRows - 1) / kPrefillRows;
+    const int staged_from = d.staged_from == 0 ? kStagedFromRows : d.staged_from;
+    if (allow_prefill && d.kv_dtype != PA_F32 && staged_from > 0 && n >= staged_from &&
+        (max_len + kPage - 1) / kPage <= kStagedMaxPages) {
+        const int64_t row_blocks = (rows + kStagedPrefillRows - 1) / kStagedPrefillRows;
         const int64_t grid = (int64_t)batch * d.num_kv_heads * row_blocks;
         if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
         pl->partition_pages = (max_len + kPage - 1) / kPage;
         pl->num_splits = 1;
-        pl->row_tiles = kPrefillRows / 16;
+        pl->row_tiles = kStagedPrefillRows / 16;
         pl->row_chunks = (int32_t)row_blocks;
         pl->waves = 4;
         pl->grid = (int32_t)grid;
@@ -1036,7 +1037,7 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
         return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_pages_per_seq");
     if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     pa_plan pl;
-    // the chunked-prefill kernel writes O in 16-byte pieces
+    // the LDS-staged kernel writes O in 8- and 16-byte pieces
     const bool out16 = reinterpret_cast<uintptr_t>(out) % 16 == 0;
     pa_status stt = make_plan(pool, batch, n, hq, max_seq_len, &pl, out16);
     if (stt != PA_OK) return stt;
@@ -1086,42 +1087,49 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
     hipError_t e;
     if (pl.kernel == 1 && tree_mask)
         return fail(PA_ERR_UNSUPPORTED, "draft trees have at most 64 nodes");
+    // draft trees on bf16 / fp8 pools: the LDS-staged kernel, 64 rows per
+    // workgroup, under the same split plan (and workspace) as the partition kernel
+    const bool staged_tree = tree_mask && d.kv_dtype != PA_F32 && d.staged_from != -1 && out16 &&
+                             pl.partition_pages <= kStagedTreeMaxPages;
     if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), st)) != hipSuccess)
         return hip_fail(e, "hipEventRecord(begin)");
-    if (pl.kernel == 1) {
-        PrefillArgs pa;
-        pa.k = d.k;
-        pa.v = d.v;
-        pa.k_scale = d.k_scale;
-        pa.v_scale = d.v_scale;
-        pa.q = static_cast<const uint16_t*>(q);
-        pa.out = static_cast<uint16_t*>(out);
-        pa.block_table = block_table;
-        pa.seq_lens = seq_lens;
-        pa.page_stride = a.page_stride;
-        pa.num_pages = d.num_pages;
-        pa.max_pages = max_pages_per_seq;
-        pa.batch = batch;
-        pa.n = n;
-        pa.hq = hq;
-        pa.hkv = d.num_kv_heads;
-        pa.group = a.group;
-        pa.rows = a.rows;
-        pa.row_blocks = pl.row_chunks;
-        pa.scale_log2 = a.scale_log2;
-        if ((e = launch_prefill(pa, d.kv_dtype == PA_FP8_E4M3, st)) != hipSuccess)
-            return hip_fail(e, "prefill kernel launch");
-        if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), st)) != hipSuccess)
-            return hip_fail(e, "hipEventRecord(end)");
-        return PA_OK;
+    if (pl.kernel == 1 || staged_tree) {
+        StagedArgs sa;
+        sa.k = d.k;
+        sa.v = d.v;
+        sa.k_scale = d.k_scale;
+        sa.v_scale = d.v_scale;
+        sa.q = static_cast<const uint16_t*>(q);
+        sa.out = static_cast<uint16_t*>(out);
+        sa.block_table = block_table;
+        sa.seq_lens = seq_lens;
+        sa.tree_mask = tree_mask;
+        sa.part_acc = a.part_acc;
+        sa.part_ml = a.part_ml;
+        sa.page_stride = a.page_stride;
+        sa.num_pages = d.num_pages;
+        sa.max_pages = max_pages_per_seq;
+        sa.batch = batch;
+        sa.n = n;
+        sa.hq = hq;
+        sa.hkv = d.num_kv_heads;
+        sa.group = a.group;
+        sa.rows = a.rows;
+        sa.row_blocks = staged_tree ? (a.rows + kStagedTreeRows - 1) / kStagedTreeRows : pl.row_chunks;
+        sa.num_splits = pl.num_splits;
+        sa.part_pages = pl.partition_pages;
+        sa.scale_log2 = a.scale_log2;
+        if ((e = launch_staged(sa, d.kv_dtype == PA_FP8_E4M3, staged_tree, st)) != hipSuccess)
+            return hip_fail(e, "staged kernel launch");
+    } else {
+        const int pf = d.prefetch > 0 ? d.prefetch : default_prefetch(d.kv_dtype, pl.row_tiles);
+        switch (d.kv_dtype) {
+        case PA_F32: launch_partition_nt<KV_F32>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
+        case PA_BF16: launch_partition_nt<KV_BF16>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
+        default: launch_partition_nt<KV_FP8>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "partition kernel launch");
     }
-    const int pf = d.prefetch > 0 ? d.prefetch : default_prefetch(d.kv_dtype, pl.row_tiles);
-    switch (d.kv_dtype) {
-    case PA_F32: launch_partition_nt<KV_F32>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
-    case PA_BF16: launch_partition_nt<KV_BF16>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
-    default: launch_partition_nt<KV_FP8>(pl.row_tiles, pl.waves, pf, a, pl.grid, st); break;
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "partition kernel launch");
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), st)) != hipSuccess)
         return hip_fail(e, "hipEventRecord(end)");
     if (pl.reduce) {
@@ -1175,7 +1183,7 @@ PA_API pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out)
     if (desc->prefetch != 0 && (desc->prefetch < 2 || desc->prefetch > 6 ||
                                 (desc->waves == 8 && desc->prefetch > 4)))
         return fail(PA_ERR_UNSUPPORTED, "prefetch must be 0, 2..6 (2..4 with 8 waves)");
-    if (desc->prefill_from < -1) return fail(PA_ERR_INVALID_ARG, "prefill_from must be >= -1");
+    if (desc->staged_from < -1) return fail(PA_ERR_INVALID_ARG, "staged_from must be >= -1");
     pa_pool* p = new (std::nothrow) pa_pool;
     if (!p) return fail(PA_ERR_INVALID_ARG, "out of host memory");
     p->d = *desc;

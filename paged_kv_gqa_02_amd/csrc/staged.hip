@@ -1,0 +1,555 @@
+// staged.hip -- attention with the KV pages staged once in LDS and shared by
+// every wave of a workgroup, for calls with many query rows per (sequence, kv
+// head): chunked prefill and draft-tree verification, on MI355X (gfx950).
+//
+// Sources: "Latency and cost in production" §10.2.6 (chunked prefill splits a
+// long prompt's prefill into chunks interleaved with decode steps) and
+// "Batching, speculative decoding, paged attention" §5.3.15 (a later chunk
+// attends again to the earlier chunks' KV) and §5.3.13 (a tree of candidate
+// branches verified in one forward with tree attention), over the block-table
+// gather of §5.3.7 and the online softmax of "Latency and cost in production"
+// §10.1.2.  The results are those of include/paged_attn.h: row i of a sequence
+// with L keys sees keys 0 .. L - n + i (causal), or every context key and its
+// draft-tree ancestors (tree).
+//
+// Design (gfx950, wave64):
+//  * a workgroup takes WAVES * TILES * 16 query rows of one (sequence, kv head)
+//    and one context partition; each wave owns TILES 16-row MFMA tiles.
+//    Chunked prefill uses 8 waves x 2 tiles (256 rows, two waves per SIMD so
+//    that one wave's softmax arithmetic overlaps the other's MFMAs), draft
+//    trees 4 waves x 1 tile (64 rows, few registers per wave);
+//  * the keys are walked in steps of two pages (32 tokens).  The workgroup
+//    copies each pair once into a ring of four LDS stages with direct
+//    global-to-LDS loads, three pairs ahead of the one being consumed, so no
+//    register holds data in flight.  Pages keep the pool's layouts: a wave's
+//    K operand is one contiguous KiB per LDS read.  E4M3 pages are converted
+//    to bf16 (exactly) as operands are read, their scales applied to the
+//    scores and probabilities.  bf16 V operands come straight from LDS with
+//    gfx950's transposing read (ds_read_b64_tr_b16), V rows being stored with
+//    a 16-byte-chunk XOR swizzle (chosen per lane in the direct copy) so that
+//    those reads are free of bank conflicts;
+//  * QK^T is v_mfma_f32_16x16x32_bf16 per page (tokens as M, rows as N); PV is
+//    the same instruction over the 32 tokens of the pair: the K index of the
+//    MFMA is free to enumerate tokens in any order, so the two pages' QK
+//    outputs, held lane by lane, are already the PV B operand, and the two
+//    pages' transposed V fragments concatenate into the A operand;
+//  * online softmax in the log2 domain with the lazy rescale of the decode
+//    kernel, the scale folded into the exponent's FMA; bf16 row sums come from
+//    one more MFMA with an all-ones operand (the sum of exactly the bf16
+//    weights that enter PV).  Per pair, both tiles' scores come first, then one
+//    rescale branch, then the weights and PV of every tile in one basic block.
+//    Only pairs that reach a row's masked keys are masked, and pairs beyond
+//    every causal row's limit are never visited;
+//  * a partition of a split sequence ends with its (max, sum, accumulator)
+//    partial in the split-K reduce kernel's layout.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "cdna4.h"
+#include "staged.h"
+
+namespace {
+
+using namespace cdna4;
+
+constexpr int kPage = 16;
+constexpr int kHeadDim = 128;
+constexpr int kSlab = kPage * kHeadDim;
+constexpr int kWave = 64;
+constexpr float kNoMax = -1.0e30f;
+// LDS ring depth in page pairs.  Four stages (three pairs in flight) keep two
+// draft-tree workgroups on a CU and the accumulators in VGPRs; deeper rings
+// measured no faster on MI355X.
+constexpr int kRing = 4;
+constexpr float kRescaleSlack = 8.0f;
+
+// One pair of pages in LDS, in the pool's layouts: [K page 0][K page 1]
+// [V page 0][V page 1], each one (page, kv head) slab of 16 * 128 elements.
+template <bool FP8, int WAVES> struct Layout {
+    static constexpr int kElem = FP8 ? 1 : 2;
+    static constexpr int kPageBytes = kSlab * kElem;            // 4 KiB bf16, 2 KiB fp8
+    static constexpr int kStage = 4 * kPageBytes;
+    static constexpr int kLoadsPerWave = kStage / 1024 / WAVES;  // 1 KiB per wave instruction
+    static_assert(kLoadsPerWave * 1024 * WAVES == kStage, "stage split over the waves");
+};
+
+// Asynchronous copy of 16 bytes per lane from global memory straight into LDS:
+// lane l's bytes (base + voff) land at lds + 16 l, so one wave instruction
+// fills 1 KiB.  base and lds are wave-uniform (scalar registers).  Issued as
+// inline assembly so that the compiler does not wait for it before every LDS
+// read; the kernel counts these loads itself (s_waitcnt vmcnt) and there are
+// no other global loads in its main loop.
+__device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t lds)
+{
+    const uint64_t addr = reinterpret_cast<uint64_t>(src);
+    // (the builtin returns a signed int: widen through uint32_t, never sign-extend)
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const uint64_t base = (uint64_t)lo | ((uint64_t)hi << 32);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_dma()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// bf16 V rows in LDS: 16-byte chunk c of row r is stored at chunk c ^ vswz(r),
+// so that the eight rows one transposing read touches fall in distinct banks.
+__device__ __forceinline__ int vswz(int row) { return 2 * (row & 7); }
+
+// Pair j into its stage, 1 KiB per wave instruction: piece p of the stage is
+// slab p / (pieces per slab) (K page 0, K page 1, V page 0, V page 1) at
+// offset 1 KiB * (p % pieces per slab); wave w copies pieces w * n .. w * n + n - 1.
+// A bf16 V piece holds rows 4i .. 4i + 3; lane l lands at row 4i + l / 16,
+// chunk l % 16, and fetches the chunk that the swizzle puts there.
+// ids[last] is the sequence's last page: a pair reaching past it repeats that
+// page (its tokens are masked and its V rows zeroed).
+template <bool FP8, int WAVES>
+__device__ __forceinline__ void issue_pair(const StagedArgs& a, const int32_t* ids, int npairs,
+                                           int last, int j, int kh, int wave, int lane,
+                                           uint32_t stage_lds)
+{
+    using Ly = Layout<FP8, WAVES>;
+    constexpr int kPieces = Ly::kPageBytes / 1024;       // per slab
+    const int jj = min(j, npairs - 1);                   // past the end: a harmless repeat
+    // both page ids of the pair in one LDS read, before any copy is issued (each
+    // copy is a compiler barrier for memory, which would re-read them); page ids
+    // are wave-uniform, so slab addresses are formed on the scalar unit
+    const int2 pp = *reinterpret_cast<const int2*>(ids + 2 * jj);
+    const int p0 = __builtin_amdgcn_readfirstlane(pp.x);
+    const int page[2] = {p0, 2 * jj + 1 <= last ? __builtin_amdgcn_readfirstlane(pp.y) : p0};
+    const uint8_t* src[Ly::kLoadsPerWave];
+    uint32_t voff[Ly::kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < Ly::kLoadsPerWave; ++i) {
+        const int piece = wave * Ly::kLoadsPerWave + i;
+        const int slab = piece / kPieces;
+        src[i] = static_cast<const uint8_t*>(slab < 2 ? a.k : a.v) +
+                 ((int64_t)page[slab & 1] * a.page_stride + (int64_t)kh * kSlab) * Ly::kElem +
+                 1024 * (piece % kPieces);
+        voff[i] = 16 * lane;
+        if (!FP8 && slab >= 2) {
+            const int row = 4 * (piece % kPieces) + (lane >> 4);
+            voff[i] = 256 * (lane >> 4) + 16 * ((lane & 15) ^ vswz(row));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < Ly::kLoadsPerWave; ++i)
+        dma16(src[i], voff[i],
+              __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (wave * Ly::kLoadsPerWave + i)));
+}
+
+// E4M3 K operand c (dims 32c + 8g .. +8 of token l16, the bf16 layout's chunk
+// 4c + g): bytes 8 (g % 2) .. +8 of fp8 chunk 2c + g / 2 of that token
+__device__ __forceinline__ u32x4 k_operand_fp8(const uint8_t* kp, int c, int l16, int g)
+{
+    const u32x2 w = *reinterpret_cast<const u32x2*>(kp + ((2 * c + (g >> 1)) * 16 + l16) * 16 +
+                                                    8 * (g & 1));
+    return fp8x8_to_bf16x8(w[0], w[1]);
+}
+
+// STAGES: LDS ring of page pairs (STAGES - 1 pairs in flight); MAXP: most
+// pages of one partition, whose page ids (and E4M3 scales) are held in LDS,
+// with the odd page its last pair may reach into the next partition.  Two
+// waves per SIMD (8 / WAVES workgroups per CU) cap a lane at 256 registers, so
+// the MFMA accumulators stay in VGPRs, where the rescale can reach them.
+template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP>
+__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_attn_staged(StagedArgs a)
+{
+    using Ly = Layout<FP8, WAVES>;
+    constexpr int kStages = STAGES;
+    constexpr int kThreads = WAVES * kWave;
+    constexpr int kRowsPerWave = 16 * TILES;
+    constexpr int kRows = WAVES * kRowsPerWave;
+    static_assert((kStages - 2) * Ly::kLoadsPerWave <= 63, "vmcnt counts at most 63 loads");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * Ly::kStage];
+    constexpr int kIds = MAXP + 2;
+    __shared__ __attribute__((aligned(8))) int32_t ids[kIds];
+    __shared__ float scales[FP8 ? 2 * kIds : 1];   // k then v, per page of the block
+
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
+
+    // blockIdx -> (split, sequence and kv head, row block): heavy row blocks
+    // first; the row blocks of one (sequence, kv head, split) share blockIdx
+    // mod (B * Hkv * splits), hence one XCD and its L2 when that is a multiple of 8
+    const int sp = blockIdx.x % a.num_splits;
+    const int rest = blockIdx.x / a.num_splits;
+    const int bh_count = a.batch * a.hkv;
+    const int bh = rest % bh_count;
+    const int rb = a.row_blocks - 1 - rest / bh_count;
+    const int kh = bh % a.hkv;
+    const int b = bh / a.hkv;
+
+    // Every load of the prologue is issued before the first one is waited for:
+    // the sequence length, this partition's block-table entries, the query rows
+    // and their tree masks (only the length decides what is used of them).
+    const int seq_len = a.seq_lens[b];
+    const int pg0 = sp * a.part_pages;
+    const int part = min(a.part_pages, MAXP);     // a larger partition is cut short
+    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+    constexpr int kIdLoads = (kIds + kThreads - 1) / kThreads;
+    int idv[kIdLoads];
+#pragma unroll
+    for (int k = 0; k < kIdLoads; ++k) {
+        const int p = t + k * kThreads;
+        idv[k] = p <= part ? bt_row[min(pg0 + p, a.max_pages - 1)] : 0;
+    }
+    const int row0 = rb * kRows;
+    const int wrow0 = row0 + wave * kRowsPerWave;
+    // query rows of this wave (MFMA B-operand layout: lane holds row l16 of a tile)
+    bf16x8 qf[TILES][4];
+    int qi[TILES];
+    uint64_t tmask[TILES];
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) {
+        const int r = wrow0 + tt * 16 + l16;
+        const bool valid = r < a.rows;
+        const int i = valid ? r / a.group : 0;
+        const int h = kh * a.group + (valid ? r - i * a.group : 0);
+        const uint16_t* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+            qf[tt][c] = __builtin_bit_cast(bf16x8, valid ? x : u32x4{0u, 0u, 0u, 0u});
+        }
+        qi[tt] = valid ? i : -1;
+        if constexpr (TREE) {
+            const uint64_t mk = a.tree_mask[(int64_t)b * a.n + i];
+            tmask[tt] = valid ? mk : ~uint64_t(0);
+        }
+    }
+
+    // lengths clamped to what the block table describes: arrays that break the
+    // contract give wrong numbers, never a stray access
+    const int L = max(min(seq_len, a.max_pages * kPage), 1);
+    const int seq_pages = (L + kPage - 1) / kPage;
+    const int nsplit_b = min((seq_pages + a.part_pages - 1) / a.part_pages, a.num_splits);
+    if (sp >= nsplit_b) return;                   // this sequence has fewer partitions
+    const int last_row = min(row0 + kRows, a.rows) - 1;
+    const int first_limit = L - a.n;              // row 0 sees tokens 0 .. L - n (causal)
+    // keys the block needs: up to the causal limit of its last row, or all (tree)
+    const int key_end = TREE ? L : max(min(L, first_limit + last_row / a.group + 1), 1);
+    const int pg_end = min(pg0 + part, (key_end + kPage - 1) / kPage);
+    const int npairs = max(pg_end - pg0 + 1, 0) / 2;
+    const int last = seq_pages - 1 - pg0;         // the sequence's last page, partition-relative
+    // the last pair of a partition with an odd page count reaches one page
+    // into the next partition: keys from here on are masked like dead ones
+    const int tok_end = min(L, kPage * pg_end);
+    int lim[TILES];
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt)
+        lim[tt] = qi[tt] >= 0 ? first_limit + qi[tt] : L - 1;   // padding rows see every live key
+    // the pairs that need masks: those past the smallest causal limit among
+    // this wave's rows, or reaching the tree tokens
+    const int wave_lim = TREE ? first_limit - 1 : first_limit + min(wrow0, a.rows - 1) / a.group;
+
+    // page ids (and E4M3 scales) of the partition, clamped to the pool
+#pragma unroll
+    for (int k = 0; k < kIdLoads; ++k) {
+        const int p = t + k * kThreads;
+        if (p < 2 * npairs) {
+            const int id = min(max(idv[k], 0), a.num_pages - 1);
+            ids[p] = id;
+            if constexpr (FP8) {
+                scales[p] = a.k_scale[(int64_t)id * a.hkv + kh];
+                scales[kIds + p] = a.v_scale[(int64_t)id * a.hkv + kh];
+            }
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc[TILES][8];
+    f32x4 lsum[TILES];      // bf16 pools: row sums of the weights, from an all-ones MFMA
+    float m[TILES], l[TILES];
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[tt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[tt] = kNoMax;
+        l[tt] = 0.f;
+    }
+    // A operand of all ones (bf16 1.0 = 0x3F80): C[m][row] = sum over the 32
+    // tokens of the row's weights, exactly the bf16 values that enter PV
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                         0x3F803F80u});
+
+    // Scores of pair jp for every tile, raw: K operands of both pages from LDS,
+    // QK^T on the MFMAs.  The scale (and an E4M3 page's K scale) is folded into
+    // the exponent later: p = exp2(s * f - m) with f > 0, so max(s * f) = f * max(s).
+    auto scores = [&](int jp, float (&sc)[TILES][8]) {
+        const uint8_t* st = lds + (jp % kStages) * Ly::kStage;
+        u32x4 kf[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint8_t* kp = st + h * Ly::kPageBytes;
+                if constexpr (FP8)
+                    kf[h][c] = k_operand_fp8(kp, c, l16, g);
+                else
+                    kf[h][c] = *reinterpret_cast<const u32x4*>(kp + 1024 * c + 16 * lane);
+            }
+#pragma unroll
+        for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[h][c]),
+                                                                 qf[tt][c], s4, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sc[tt][4 * h + v] = s4[v];
+            }
+    };
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    if (npairs > 0) {
+        // prologue: pairs 0 .. kStages - 2 in flight (past the end: repeats)
+#pragma unroll
+        for (int j = 0; j < kStages - 1; ++j)
+            issue_pair<FP8, WAVES>(a, ids, npairs, last, j, kh, wave, lane, lds0 + j * Ly::kStage);
+    }
+
+    for (int j = 0; j < npairs; ++j) {
+        // this wave's part of pair j has landed once at most the later pairs'
+        // loads are outstanding; the barrier then covers every wave's part, and
+        // every wave is done with pair j - 1, whose stage is refilled next
+        wait_dma<(kStages - 2) * Ly::kLoadsPerWave>();
+        __syncthreads();
+        issue_pair<FP8, WAVES>(a, ids, npairs, last, j + kStages - 1, kh, wave, lane,
+                               lds0 + ((j + kStages - 1) % kStages) * Ly::kStage);
+
+        uint8_t* st = lds + (j % kStages) * Ly::kStage;
+        const int base = 16 * pg0 + 32 * j;       // first token of the pair
+        const bool need_mask = base + 31 > wave_lim || base + 31 >= tok_end;
+        if (base + 31 >= L) {
+            // the pair holding the sequence end: V rows past it may hold NaN,
+            // which a zero weight would still carry through the MFMA, so they
+            // are zeroed in LDS (once per workgroup, on this pair only)
+            constexpr int kRowBytes = kHeadDim * Ly::kElem;
+            for (int e = t; e < 32 * kRowBytes / 16; e += WAVES * kWave) {
+                const int tok = e / (kRowBytes / 16);
+                if (base + tok >= L)
+                    *reinterpret_cast<u32x4*>(st + (2 + tok / 16) * Ly::kPageBytes +
+                                              (tok % 16) * kRowBytes + 16 * (e % (kRowBytes / 16))) =
+                        u32x4{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();
+        }
+        float sc[TILES][8];
+        scores(j, sc);
+        float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
+        if constexpr (FP8) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int pg = min(2 * j + h, last);
+                ks[h] = scales[pg];
+                vs[h] = scales[kIds + pg];
+            }
+        }
+        // V operands over the 32 tokens: {page 0 rows 4g..4g+3, page 1 rows 4g..4g+3}
+        bf16x8 va[8];
+        {
+            i16x4 av[2][8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint8_t* vp = st + (2 + h) * Ly::kPageBytes;
+                if constexpr (FP8) {
+                    // a[db] = {V[4g + s][8 l16 + db], s = 0..3}: rows read, then permuted
+                    u32x4 vr[4];
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(vp + (4 * g + s4) * kHeadDim + 8 * l16);
+                        vr[s4] = fp8x8_to_bf16x8(w[0], w[1]);
+                    }
+                    v_operands(av[h], vr);
+                } else {
+                    // a[db] = {V[4g + k][16 db + l16], k = 0..3} from one transposing
+                    // read: in each 16-lane group, lane j names 4 elements of row
+                    // 4g + j / 4 at dims 16 db + 4 (j % 4), and lane i receives the
+                    // i % 4-th element of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4
+                    const int row = 4 * g + (l16 >> 2);
+                    const uint8_t* rp = vp + 2 * kHeadDim * row + 8 * (l16 & 1);
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) {
+                        const int chunk = 2 * db + ((l16 & 3) >> 1);
+                        av[h][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(rp + 16 * (chunk ^ vswz(row))));
+                    }
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                va[db] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(av[0][db], av[1][db], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        float f[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) f[h] = FP8 ? a.scale_log2 * ks[h] : a.scale_log2;
+        if (need_mask) {
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tok = base + 16 * (e >> 2) + 4 * g + (e & 3);
+                    bool vis;
+                    if constexpr (TREE)
+                        vis = tok < first_limit ||
+                              ((tmask[tt] >> min(max(tok - first_limit, 0), 63)) & 1u);
+                    else
+                        vis = tok <= lim[tt];
+                    vis = vis && tok < tok_end;
+                    sc[tt][e] = vis ? sc[tt][e] : -INFINITY;
+                }
+        }
+        // Phase 2: row maxima, and one rescale branch for all tiles (a tile
+        // whose maximum did not move is multiplied by exp2(0) = 1, exactly)
+        float mx[TILES];
+        bool grow_any = false;
+#pragma unroll
+        for (int tt = 0; tt < TILES; ++tt) {
+            float x = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float ph = fmaxf(fmaxf(sc[tt][4 * h], sc[tt][4 * h + 1]),
+                                       fmaxf(sc[tt][4 * h + 2], sc[tt][4 * h + 3]));
+                x = fmaxf(x, ph * f[h]);
+            }
+            mx[tt] = group_max(x);
+            grow_any |= mx[tt] > m[tt] + kRescaleSlack;
+        }
+        if (__any(grow_any)) {
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+                const float mnew = mx[tt] > m[tt] + kRescaleSlack ? mx[tt] : m[tt];
+                const float alpha = fast_exp2(m[tt] - mnew);
+                m[tt] = mnew;
+                l[tt] *= alpha;
+                lsum[tt] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) acc[tt][db] *= alpha;
+            }
+        }
+        // Phase 3, one basic block: weights and PV of every tile, so that one
+        // tile's exponentials can issue while the other's MFMAs run
+#pragma unroll
+        for (int tt = 0; tt < TILES; ++tt) {
+            float pw[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = fast_exp2(__builtin_fmaf(sc[tt][e], f[e >> 2], -m[tt]));
+                pw[e] = FP8 ? p * vs[e >> 2] : p;
+                if constexpr (FP8) psum += p;
+            }
+            const bf16x8 pf = __builtin_bit_cast(
+                bf16x8, u32x4{bf16x2_bits(pw[0], pw[1]), bf16x2_bits(pw[2], pw[3]),
+                              bf16x2_bits(pw[4], pw[5]), bf16x2_bits(pw[6], pw[7])});
+            if constexpr (FP8)
+                l[tt] += psum;      // the V scale rides on the weights, not on their sum
+            else
+                lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[tt], 0, 0, 0);
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                acc[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, acc[tt][db], 0, 0, 0);
+        }
+    }
+    // no copy may still be writing this workgroup's LDS when it exits
+    wait_dma<0>();
+
+    // epilogue: lane holds O[row l16][32 g + 8 v + db] (E4M3 pools) or
+    // O[row l16][16 db + 4 g + v] (bf16 pools) of each tile; the final output
+    // when the sequence has one partition, else this partition's partial
+    const bool single = nsplit_b == 1;
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) {
+        const int r = wrow0 + tt * 16 + l16;
+        const float lt = FP8 ? group_sum(l[tt]) : lsum[tt][0];
+        if (r < a.rows) {
+            const int i = r / a.group;
+            const int h = kh * a.group + (r - i * a.group);
+            const int64_t orow = ((int64_t)b * a.n + i) * a.hq + h;
+            if (single) {
+                const float inv = 1.0f / lt;
+                uint16_t* o = a.out + orow * kHeadDim;
+                if constexpr (FP8) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        uint32_t w[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            w[e] = bf16x2_bits(acc[tt][2 * e][v] * inv, acc[tt][2 * e + 1][v] * inv);
+                        *reinterpret_cast<u32x4*>(o + 32 * g + 8 * v) = u32x4{w[0], w[1], w[2], w[3]};
+                    }
+                } else {
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) {
+                        const f32x4 x = acc[tt][db] * inv;
+                        *reinterpret_cast<u32x2*>(o + 16 * db + 4 * g) =
+                            u32x2{bf16x2_bits(x[0], x[1]), bf16x2_bits(x[2], x[3])};
+                    }
+                }
+            } else {
+                const int64_t pidx = orow * a.num_splits + sp;
+                float* pa = a.part_acc + pidx * kHeadDim;
+                if constexpr (FP8) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        f32x4 lo, hi;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            lo[e] = acc[tt][e][v];
+                            hi[e] = acc[tt][4 + e][v];
+                        }
+                        *reinterpret_cast<f32x4*>(pa + 32 * g + 8 * v) = lo;
+                        *reinterpret_cast<f32x4*>(pa + 32 * g + 8 * v + 4) = hi;
+                    }
+                } else {
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+                        *reinterpret_cast<f32x4*>(pa + 16 * db + 4 * g) = acc[tt][db];
+                }
+                if (g == 0) {
+                    a.part_ml[pidx * 2] = m[tt];
+                    a.part_ml[pidx * 2 + 1] = lt;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+namespace {
+
+template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP>
+hipError_t launch(const StagedArgs& a, dim3 grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((paged_attn_staged<FP8, WAVES, TILES, TREE, STAGES, MAXP>), grid,
+                       dim3(WAVES * kWave), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st)
+{
+    const dim3 grid((unsigned)((int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits));
+    if (tree)
+        return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st)
+                   : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st);
+    return fp8 ? launch<true, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st)
+               : launch<false, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st);
+}

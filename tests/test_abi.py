@@ -34,7 +34,7 @@ def test_status_strings():
 def _desc(**kw):
     d = dict(num_pages=64, page_size=16, num_kv_heads=8, head_dim=128, kv_dtype=B.PA_BF16,
              k=FAKE_K, v=FAKE_V, k_scale=None, v_scale=None, partition_pages=0, waves=0,
-             prefetch=0, prefill_from=0)
+             prefetch=0, staged_from=0)
     d.update(kw)
     return B.pa_pool_desc(**d)
 
@@ -57,7 +57,7 @@ def _create(**kw):
     (dict(waves=6), B.PA_ERR_UNSUPPORTED),
     (dict(prefetch=9), B.PA_ERR_UNSUPPORTED),
     (dict(waves=8, prefetch=5), B.PA_ERR_UNSUPPORTED),
-    (dict(prefill_from=-2), B.PA_ERR_INVALID_ARG),
+    (dict(staged_from=-2), B.PA_ERR_INVALID_ARG),
 ])
 def test_create_pool_rejects(kw, status):
     st, h = _create(**kw)
@@ -104,10 +104,10 @@ def test_prefill_plans():
     assert LIB.paged_attn_workspace_bytes(h, 4, 512, 32, 2048, ctypes.byref(ws)) == 0
     assert ws.value == 0
     LIB.paged_attn_destroy_pool(h)
-    st, h = _create(num_pages=8192, prefill_from=-1)  # never
+    st, h = _create(num_pages=8192, staged_from=-1)  # never
     assert _plan(h, 4, 512, 32, 2048).kernel == 0
     LIB.paged_attn_destroy_pool(h)
-    st, h = _create(num_pages=8192, prefill_from=16)
+    st, h = _create(num_pages=8192, staged_from=16)
     assert _plan(h, 4, 16, 32, 2048).kernel == 1
     LIB.paged_attn_destroy_pool(h)
     st, h = _create(num_pages=8192, kv_dtype=B.PA_F32)   # fp32 stays on the partition kernel

@@ -33,13 +33,15 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_gpu(pa, case, partition_pages=0, dev=None, label="", waves=0, prefetch=0):
+def run_gpu(pa, case, partition_pages=0, dev=None, label="", waves=0, prefetch=0,
+            staged_from=0):
     say(f"[gpu] {case.name} {label} kv={case.kv_dtype} B={case.batch} n={case.q_per_seq} "
         f"Hq={case.num_q_heads} Hkv={case.num_kv_heads} maxL={case.max_seq_len} "
-        f"part={partition_pages} waves={waves} prefetch={prefetch} seed={case.seed}")
+        f"part={partition_pages} waves={waves} prefetch={prefetch} staged_from={staged_from} "
+        f"seed={case.seed}")
     d = dev if dev is not None else to_device(case)
     pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale, partition_pages, waves,
-                                     prefetch)
+                                     prefetch, staged_from)
     out = torch.empty_like(d.q)
     ws = pa.workspace_for(pool, d.q, case.max_seq_len)
     pa.paged_attn_verify(pool, d.q, out, d.block_table, d.seq_lens, case.max_seq_len,
@@ -339,24 +341,44 @@ def with_tree(case, seed):
     return case
 
 
+@pytest.mark.parametrize("kernel", ["staged", "partition"])
 @pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("n", [5, 16, 64])
-def test_tree_verify_matches_oracle(pa, kv, n):
+def test_tree_verify_matches_oracle(pa, kernel, kv, n):
+    # bf16 / fp8 trees take the LDS-staged kernel unless staged_from = -1; f32 never
     case = with_tree(small_case(kv, n, 32, 8, [n, n + 17, 300, 1000], seed=200 + n), 300 + n)
     ref = run_oracle(case)
     dev = to_device(case)
-    for part in (0, 3):
-        check(run_gpu(pa, case, part, dev=dev, label="tree"), ref, kv, f"tree n={n} part={part}")
+    sf = 0 if kernel == "staged" else -1
+    for part in (0, 3, 4):      # odd and even partition lengths
+        check(run_gpu(pa, case, part, dev=dev, label=f"tree {kernel}", staged_from=sf), ref, kv,
+              f"tree n={n} part={part} {kernel}")
 
 
 @pytest.mark.parametrize("n", [5, 16])
 def test_chain_tree_equals_causal_verify_bitwise(pa, n):
+    """On one kernel (the partition kernel takes both), a chain tree is the causal mask."""
     case = small_case("bf16", n, 32, 8, [4101, 77, n], seed=210 + n)
     dev = to_device(case)
-    causal = run_gpu(pa, case, dev=dev, label="causal")
+    causal = run_gpu(pa, case, dev=dev, label="causal", staged_from=-1)
     case.tree_mask = np.stack([W.chain_tree(n)] * case.batch)
-    chain = run_gpu(pa, case, label="chain tree")
+    chain = run_gpu(pa, case, label="chain tree", staged_from=-1)
     assert (chain == causal).all()
+
+
+@pytest.mark.parametrize("n", [5, 16, 64])
+def test_staged_chain_tree_equals_causal_verify(pa, n):
+    """The LDS-staged tree kernel on a chain tree against the causal verify."""
+    case = small_case("bf16", n, 32, 8, [4101, 77, n], seed=230 + n)
+    dev = to_device(case)
+    causal = run_gpu(pa, case, dev=dev, label="causal", staged_from=-1)
+    case.tree_mask = np.stack([W.chain_tree(n)] * case.batch)
+    for part in (0, 5):
+        chain = run_gpu(pa, case, part, label="staged chain tree")
+        # two kernels, two fp32 accumulation orders, each rounded to bf16, so
+        # the same bf16 gate each of them meets against the oracle (outputs
+        # here reach O(1), where one bf16 ulp is 2^-7)
+        check(chain, causal, "bf16", f"staged chain tree vs causal part={part}")
 
 
 def test_tree_entry_point_and_limits(pa):

@@ -2,7 +2,7 @@
 sequence, each attending to the earlier chunks' keys and causally within its
 own chunk.  Every case runs through the chunked-prefill kernel (the automatic
 choice from 128 rows per sequence) and through the partition kernel
-(prefill_from = -1), against the oracle; at the full workload also against the
+(staged_from = -1), against the oracle; at the full workload also against the
 pin that prefill row i is the decode of the same query at length L - n + i + 1.
 """
 import numpy as np
@@ -15,7 +15,7 @@ from test_gpu_parity import MAX_ABS, check, run_oracle, say, small_case
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = {"prefill": 0, "partition": -1}      # pool prefill_from
+KERNELS = {"prefill": 0, "partition": -1}      # pool staged_from
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def pa():
 def run(pa, case, kernel, dev=None):
     d = dev if dev is not None else to_device(case)
     pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale,
-                                     prefill_from=KERNELS[kernel])
+                                     staged_from=KERNELS[kernel])
     plan = pa.paged_attn_plan(pool, case.batch, case.q_per_seq, case.num_q_heads,
                               case.max_seq_len)
     say(f"[gpu prefill] {case.name} kernel={kernel} (plan {plan['kernel']}) kv={case.kv_dtype} "

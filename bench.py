@@ -10,7 +10,10 @@ reads rather than writes: a written buffer leaves dirty lines in the MALL
 whose write-back would then compete with the timed kernel for HBM.
 
 Prints ONE JSON line (rank 0).  `value` is effective HBM GB/s: (K + V bytes of
-every token of every sequence, fp8 scales, Q, O) / mean call time.
+every token of every sequence, fp8 scales, Q, O) / mean call time, the call
+bracketed by two HIP events on its stream.  `roofline.achieved` divides the
+same bytes by the attention kernel's own execution time, from events the
+library attaches to that kernel's dispatch (paged_attn_verify_timed).
 
 `--op append` instead times paged_attn_append_kv, the step before attention:
 the n_new newest tokens of every sequence of the workload (default: its query
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode8b", choices=W.WORKLOADS)
     ap.add_argument("--partition-pages", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0, help="pool knob: waves per workgroup")
+    ap.add_argument("--prefetch", type=int, default=0, help="pool knob: pages in flight per wave")
     ap.add_argument("--staged-from", type=int, default=0,
                     help="pool knob: rows per sequence from which causal calls take the "
                          "LDS-staged kernel (0 = library default, -1 = never)")
@@ -358,7 +363,8 @@ def main():
     case = W.workload(args.workload)
     dev = to_device(case)
     pool = pa.paged_attn_create_pool(dev.k, dev.v, dev.k_scale, dev.v_scale,
-                                     args.partition_pages, staged_from=args.staged_from)
+                                     args.partition_pages, args.waves, args.prefetch,
+                                     staged_from=args.staged_from)
     plan = pa.paged_attn_plan(pool, case.batch, case.q_per_seq, case.num_q_heads,
                               case.max_seq_len)
     out = torch.empty_like(dev.q)
@@ -380,33 +386,27 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K steps, each = cache flush + one call bracketed by HIP
-    # events on the stream the kernels run on.  Without a split the call is
-    # the partition kernel alone and the library records the events right
-    # around it; with a split, events bracket the call and a second pass
-    # below times the partition kernel by itself.
+    # events recorded on the stream the kernels run on (the events' own
+    # latency counts against the call).  A second pass of the same length
+    # times the attention kernel alone: the library attaches the events to
+    # that kernel's dispatch, so they hold its start and end times.
     evs = [(pa.HipEvent(), pa.HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e0, e1 in evs:
         flush_caches()
-        if plan["reduce"]:
-            e0.record(stream)
-            call()
-            e1.record(stream)
-        else:
-            call(e0, e1)
+        e0.record(stream)
+        call()
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     call_ms = np.array([e0.elapsed_ms(e1) for e0, e1 in evs])
-    if plan["reduce"]:
-        kevs = [(pa.HipEvent(), pa.HipEvent()) for _ in range(args.steps)]
-        for e0, e1 in kevs:
-            flush_caches()
-            call(e0, e1)
-        torch.cuda.synchronize()
-        kern_ms = np.array([e0.elapsed_ms(e1) for e0, e1 in kevs])
-    else:
-        kern_ms = call_ms
+    kevs = [(pa.HipEvent(), pa.HipEvent()) for _ in range(args.steps)]
+    for e0, e1 in kevs:
+        flush_caches()
+        call(e0, e1)
+    torch.cuda.synchronize()
+    kern_ms = np.array([e0.elapsed_ms(e1) for e0, e1 in kevs])
     log(f"timed {args.steps} steps: call {call_ms.mean() * 1e3:.1f} us, "
         f"attention kernel {kern_ms.mean() * 1e3:.1f} us")
 

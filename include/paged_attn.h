@@ -183,10 +183,11 @@ pa_status paged_attn_verify_tree(const pa_pool* pool, const void* q, pa_dtype q_
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* paged_attn_verify (tree_mask NULL) or paged_attn_verify_tree (tree_mask set)
- * that also records ev_begin right before the attention (partition) kernel and
- * ev_end right after it on the same stream, so a caller can time that kernel
- * alone.  The events are hipEvent_t handles created by the caller; either may
- * be NULL. */
+ * that also times the attention kernel (partition or LDS-staged; not the
+ * split-K reduce): the events are attached to that kernel's own dispatch and
+ * take the times at which it starts and ends, so hipEventElapsedTime gives its
+ * execution time with no marker overhead.  The events are hipEvent_t handles
+ * created by the caller; either may be NULL. */
 pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q_dtype,
                                   void* out, const int32_t* block_table,
                                   int32_t max_pages_per_seq, const int32_t* seq_lens,

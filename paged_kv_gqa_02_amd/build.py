@@ -9,7 +9,8 @@ import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "staged.hip", "spec_sample.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("paged_attn.hip", "decode.hip", "append.hip", "staged.hip",
+                                                      "spec_sample.hip")]
 LIB = os.path.join(PKG, "libpaged_attn.so")
 INCLUDE = os.path.join(ROOT, "include")
 

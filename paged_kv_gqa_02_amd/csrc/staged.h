@@ -41,4 +41,6 @@ constexpr int kStagedTreeRows = 64;
 constexpr int kStagedMaxPages = 2048;
 constexpr int kStagedTreeMaxPages = 512;
 // Launches the kernel on `st`; grid = batch * hkv * row_blocks * num_splits.
-hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st);
+// ev_begin / ev_end (either may be null) take the kernel's start and end times.
+hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st,
+                         hipEvent_t ev_begin, hipEvent_t ev_end);

@@ -42,6 +42,7 @@
 //    every causal row's limit are never visited;
 //  * a partition of a split sequence ends with its (max, sum, accumulator)
 //    partial in the split-K reduce kernel's layout.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -156,11 +157,12 @@ __device__ __forceinline__ u32x4 k_operand_fp8(const uint8_t* kp, int c, int l16
 
 // STAGES: LDS ring of page pairs (STAGES - 1 pairs in flight); MAXP: most
 // pages of one partition, whose page ids (and E4M3 scales) are held in LDS,
-// with the odd page its last pair may reach into the next partition.  Two
-// waves per SIMD (8 / WAVES workgroups per CU) cap a lane at 256 registers, so
-// the MFMA accumulators stay in VGPRs, where the rescale can reach them.
+// with the odd page its last pair may reach into the next partition.  Asking
+// for at least two waves per SIMD caps a lane at 256 registers, so the MFMA
+// accumulators stay in VGPRs, where the rescale can reach them (in AGPRs they
+// would be copied out and back on every pair).
 template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP>
-__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_attn_staged(StagedArgs a)
+__global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs a)
 {
     using Ly = Layout<FP8, WAVES>;
     constexpr int kStages = STAGES;
@@ -535,21 +537,22 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_attn_staged(St
 namespace {
 
 template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP>
-hipError_t launch(const StagedArgs& a, dim3 grid, hipStream_t st)
+hipError_t launch(const StagedArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    hipLaunchKernelGGL((paged_attn_staged<FP8, WAVES, TILES, TREE, STAGES, MAXP>), grid,
-                       dim3(WAVES * kWave), 0, st, a);
+    hipExtLaunchKernelGGL((paged_attn_staged<FP8, WAVES, TILES, TREE, STAGES, MAXP>), grid,
+                          dim3(WAVES * kWave), 0, st, e0, e1, 0, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st)
+hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st,
+                         hipEvent_t e0, hipEvent_t e1)
 {
     const dim3 grid((unsigned)((int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits));
     if (tree)
-        return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st)
-                   : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st);
-    return fp8 ? launch<true, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st)
-               : launch<false, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st);
+        return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st, e0, e1)
+                   : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st, e0, e1);
+    return fp8 ? launch<true, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1)
+               : launch<false, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1);
 }

@@ -420,3 +420,34 @@ def test_workload_fp32_structure(pa, name):
 def test_workload_one_hot(pa, name):
     case = W.workload(name, poison=True)
     check_one_hot(pa, case, name)
+
+
+@pytest.mark.parametrize("kind", ["partition", "staged tree", "split partition"])
+def test_timed_call_same_output_and_kernel_time(pa, kind):
+    """paged_attn_verify_timed: the same bits as the untimed call, and the
+    events attached to the attention kernel's dispatch give its execution time,
+    which lies inside the time of events recorded around the whole call."""
+    n = 16 if kind == "staged tree" else 1
+    case = small_case("bf16", n, 32, 8, [1500, 700, 33], seed=77)
+    if kind == "staged tree":
+        rng = np.random.default_rng(78)
+        case.tree_mask = np.stack([W.random_tree(rng, n)[1] for _ in range(case.batch)])
+    d = to_device(case)
+    part = 16 if kind == "split partition" else 0
+    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale, part)
+    ws = pa.workspace_for(pool, d.q, case.max_seq_len)
+    plain = torch.empty_like(d.q)
+    pa.paged_attn_verify(pool, d.q, plain, d.block_table, d.seq_lens, case.max_seq_len,
+                         case.scale, ws, tree_mask=d.tree_mask)
+    timed = torch.empty_like(d.q)
+    stream = torch.cuda.current_stream()
+    c0, c1, k0, k1 = (pa.HipEvent() for _ in range(4))
+    c0.record(stream)
+    pa.paged_attn_verify(pool, d.q, timed, d.block_table, d.seq_lens, case.max_seq_len,
+                         case.scale, ws, ev_begin=k0, ev_end=k1, tree_mask=d.tree_mask)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), timed.view(torch.int16))
+    kern, call = k0.elapsed_ms(k1), c0.elapsed_ms(c1)
+    say(f"    {kind}: kernel {kern * 1e3:.2f} us inside call {call * 1e3:.2f} us")
+    assert 0 < kern <= call

@@ -116,8 +116,10 @@ typedef struct pa_plan {
     int32_t grid;             /* workgroups of the partition kernel */
     int32_t reduce;           /* 1 if the split-K reduce kernel runs */
     int32_t kernel;           /* 0: partition kernel (+ reduce); 1: LDS-staged kernel for
-                                 chunked prefill (256 rows of one sequence and kv head per
-                                 workgroup, no split, no workspace).  Draft-tree calls on
+                                 chunked prefill (128 rows of one sequence and kv head per
+                                 workgroup; one partition per sequence and no workspace,
+                                 unless the pool's partition_pages asks for shorter
+                                 partitions, which then take the reduce).  Draft-tree calls on
                                  bf16 / fp8 pools run the LDS-staged kernel with 64 rows per
                                  workgroup under the split plan reported here. */
 } pa_plan;

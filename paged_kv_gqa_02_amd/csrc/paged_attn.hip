@@ -99,15 +99,20 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     if (allow_prefill && d.kv_dtype != PA_F32 && staged_from > 0 && n >= staged_from &&
         (max_len + kPage - 1) / kPage <= kStagedMaxPages) {
         const int64_t row_blocks = (rows + kStagedPrefillRows - 1) / kStagedPrefillRows;
-        const int64_t grid = (int64_t)batch * d.num_kv_heads * row_blocks;
+        const int max_pages = (max_len + kPage - 1) / kPage;
+        int part = max_pages;
+        if (d.partition_pages > 0) part = std::min(d.partition_pages, max_pages);
+        part = std::max(part, (max_pages + kMaxSplits - 1) / kMaxSplits);
+        const int64_t ns = (max_pages + part - 1) / part;
+        const int64_t grid = (int64_t)batch * d.num_kv_heads * row_blocks * ns;
         if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
-        pl->partition_pages = (max_len + kPage - 1) / kPage;
-        pl->num_splits = 1;
+        pl->partition_pages = part;
+        pl->num_splits = (int32_t)ns;
         pl->row_tiles = kStagedPrefillRows / 16;
         pl->row_chunks = (int32_t)row_blocks;
         pl->waves = 4;
         pl->grid = (int32_t)grid;
-        pl->reduce = 0;
+        pl->reduce = ns > 1 ? 1 : 0;
         pl->kernel = 1;
         return PA_OK;
     }

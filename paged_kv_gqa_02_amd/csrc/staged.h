@@ -34,7 +34,7 @@ struct StagedArgs {
 };
 
 // rows of one (sequence, kv head) per workgroup: chunked prefill, draft trees
-constexpr int kStagedPrefillRows = 256;
+constexpr int kStagedPrefillRows = 128;
 constexpr int kStagedTreeRows = 64;
 // pages one workgroup can address (their page ids are staged in LDS): chunked
 // prefill (one partition per sequence), draft-tree partitions

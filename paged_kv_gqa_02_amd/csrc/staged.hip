@@ -15,9 +15,10 @@
 // Design (gfx950, wave64):
 //  * a workgroup takes WAVES * TILES * 16 query rows of one (sequence, kv head)
 //    and one context partition; each wave owns TILES 16-row MFMA tiles.
-//    Chunked prefill uses 8 waves x 2 tiles (256 rows, two waves per SIMD so
-//    that one wave's softmax arithmetic overlaps the other's MFMAs), draft
-//    trees 4 waves x 1 tile (64 rows, few registers per wave);
+//    Chunked prefill uses 4 waves x 2 tiles (128 rows; two workgroups per CU,
+//    so that one wave's softmax arithmetic overlaps another's MFMAs, and the
+//    unequal row blocks of sequences at different chunk stages share CUs),
+//    draft trees 4 waves x 1 tile (64 rows, few registers per wave);
 //  * the keys are walked in steps of two pages (32 tokens).  The workgroup
 //    copies each pair once into a ring of four LDS stages with direct
 //    global-to-LDS loads, three pairs ahead of the one being consumed, so no
@@ -302,6 +303,10 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
                 else
                     kf[h][c] = *reinterpret_cast<const u32x4*>(kp + 1024 * c + 16 * lane);
             }
+        // MFMA runs at raised wave priority, here and for PV: a wave about to
+        // issue MFMAs goes first, and the other waves of the SIMD fill its
+        // MFMA time with their softmax arithmetic (about 2 % on prefill)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
@@ -314,6 +319,7 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
 #pragma unroll
                 for (int v = 0; v < 4; ++v) sc[tt][4 * h + v] = s4[v];
             }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -463,9 +469,11 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
                 l[tt] += psum;      // the V scale rides on the weights, not on their sum
             else
                 lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[tt], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int db = 0; db < 8; ++db)
                 acc[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, acc[tt][db], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     // no copy may still be writing this workgroup's LDS when it exits
@@ -553,6 +561,6 @@ hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t s
     if (tree)
         return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st, e0, e1)
                    : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st, e0, e1);
-    return fp8 ? launch<true, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1)
-               : launch<false, 8, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1);
+    return fp8 ? launch<true, 4, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1)
+               : launch<false, 4, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1);
 }

@@ -95,10 +95,10 @@ def test_plans_for_named_workloads():
 def test_prefill_plans():
     st, h = _create(num_pages=8192)
     pre = _plan(h, 4, 512, 32, 2048)                 # 2048 rows -> 8 blocks of 256, no split
-    assert pre.kernel == 1 and pre.row_chunks == 8 and pre.grid == 4 * 8 * 8
+    assert pre.kernel == 1 and pre.row_chunks == 16 and pre.grid == 4 * 8 * 16
     assert pre.reduce == 0 and pre.num_splits == 1
     assert _plan(h, 4, 127, 32, 2048).kernel == 0    # below 128 rows per sequence
-    assert _plan(h, 1, 130, 32, 2048).row_chunks == 3    # 520 rows: the last block partial
+    assert _plan(h, 1, 130, 32, 2048).row_chunks == 5    # 520 rows: the last block partial
     assert _plan(h, 1, 128, 32, 2048 * 16 + 16).kernel == 0   # past the page-id table
     ws = ctypes.c_size_t(1)
     assert LIB.paged_attn_workspace_bytes(h, 4, 512, 32, 2048, ctypes.byref(ws)) == 0

@@ -26,13 +26,14 @@ def pa():
     return lib
 
 
-def run(pa, case, kernel, dev=None):
+def run(pa, case, kernel, dev=None, partition_pages=0):
     d = dev if dev is not None else to_device(case)
-    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale,
+    pool = pa.paged_attn_create_pool(d.k, d.v, d.k_scale, d.v_scale, partition_pages,
                                      staged_from=KERNELS[kernel])
     plan = pa.paged_attn_plan(pool, case.batch, case.q_per_seq, case.num_q_heads,
                               case.max_seq_len)
-    say(f"[gpu prefill] {case.name} kernel={kernel} (plan {plan['kernel']}) kv={case.kv_dtype} "
+    say(f"[gpu prefill] {case.name} kernel={kernel} (plan {plan['kernel']}, "
+        f"{plan['num_splits']} splits) kv={case.kv_dtype} "
         f"B={case.batch} n={case.q_per_seq} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
         f"lens={list(case.seq_lens)} seed={case.seed}")
     want = 1 if kernel == "prefill" and case.kv_dtype != "f32" else 0
@@ -118,3 +119,16 @@ def test_prefill_rows_are_stacked_decodes(pa):
         worst = max(worst, float(diff))
     say(f"    prefill rows vs decode: max_abs={worst:.3e}")
     assert worst <= MAX_ABS["bf16"]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("part", [3, 8])
+def test_prefill_kernel_split_partitions(pa, kv, part):
+    """Shorter partitions asked through the pool: the staged kernel writes split-K
+    partials (odd partition lengths reach one page into the next partition, and
+    row blocks whose causal limit ends before a partition write empty partials),
+    and the reduce merges them."""
+    n = 200
+    case = small_case(kv, n, 32, 8, [n, n + 333, n + 16 * 9 + 5], seed=930 + part)
+    check(run(pa, case, "prefill", partition_pages=part), run_oracle(case), kv,
+          f"prefill split part={part} {kv}")

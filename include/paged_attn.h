@@ -137,11 +137,15 @@ pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out);
 /* Frees the handle only; the pool arrays stay with the caller.  NULL is a no-op. */
 void paged_attn_destroy_pool(pa_pool* pool);
 
-/* The split the library will use for a call of this shape (host only). */
+/* The split the library will use for a causal call of this shape (host only).
+ * A draft-tree call never takes the chunked-prefill plan (kernel = 1): where
+ * this reports it (q_per_seq at or above a pool's staged_from of 64 or less),
+ * the tree call runs the split plan computed without it. */
 pa_status paged_attn_plan(const pa_pool* pool, int32_t batch, int32_t q_per_seq,
                           int32_t num_q_heads, int32_t max_seq_len, pa_plan* plan);
 
-/* Workspace bytes a call of this shape needs (0 when it runs unsplit). */
+/* Workspace bytes a call of this shape needs (0 when it runs unsplit); the
+ * same buffer serves the causal and the draft-tree call of the shape. */
 pa_status paged_attn_workspace_bytes(const pa_pool* pool, int32_t batch,
                                      int32_t q_per_seq, int32_t num_q_heads,
                                      int32_t max_seq_len, size_t* bytes);

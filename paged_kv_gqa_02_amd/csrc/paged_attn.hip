@@ -181,9 +181,10 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
         return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_pages_per_seq");
     if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     pa_plan pl;
-    // the LDS-staged kernel writes O in 8- and 16-byte pieces
+    // the LDS-staged kernel writes O in 8- and 16-byte pieces; draft trees
+    // never take the chunked-prefill plan (they have their own staged path)
     const bool out16 = reinterpret_cast<uintptr_t>(out) % 16 == 0;
-    pa_status stt = make_plan(pool, batch, n, hq, max_seq_len, &pl, out16);
+    pa_status stt = make_plan(pool, batch, n, hq, max_seq_len, &pl, out16 && !tree_mask);
     if (stt != PA_OK) return stt;
     const size_t need = workspace_for(pl, batch, n, hq);
     if (need > 0) {
@@ -229,8 +230,6 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (pl.kernel == 1 && tree_mask)
-        return fail(PA_ERR_UNSUPPORTED, "draft trees have at most 64 nodes");
     // draft trees on bf16 / fp8 pools: the LDS-staged kernel, 64 rows per
     // workgroup, under the same split plan (and workspace) as the partition kernel
     const bool staged_tree = tree_mask && d.kv_dtype != PA_F32 && d.staged_from != -1 && out16 &&
@@ -337,10 +336,15 @@ PA_API pa_status paged_attn_workspace_bytes(const pa_pool* pool, int32_t batch, 
                                             size_t* bytes)
 {
     if (!bytes) return fail(PA_ERR_INVALID_ARG, "null output pointer");
-    pa_plan pl;
+    // enough for the causal call of this shape and for the draft-tree call,
+    // which never takes the chunked-prefill plan
+    pa_plan pl, tree;
     pa_status st = make_plan(pool, batch, q_per_seq, num_q_heads, max_seq_len, &pl);
     if (st != PA_OK) return st;
-    *bytes = workspace_for(pl, batch, q_per_seq, num_q_heads);
+    st = make_plan(pool, batch, q_per_seq, num_q_heads, max_seq_len, &tree, false);
+    if (st != PA_OK) return st;
+    *bytes = std::max(workspace_for(pl, batch, q_per_seq, num_q_heads),
+                      workspace_for(tree, batch, q_per_seq, num_q_heads));
     return PA_OK;
 }
 

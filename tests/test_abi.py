@@ -209,3 +209,23 @@ def test_sample_workspace_bytes():
 def test_sample_rejects_before_launch(kw, status):
     assert _sample(**kw) == status
     assert LIB.paged_attn_last_error()
+
+
+def test_workspace_covers_tree_calls_when_prefill_plan_is_reported():
+    """staged_from = 16: a 20-row shape reports the chunked-prefill plan (no
+    workspace), but a draft-tree call of that shape runs the split plan, so the
+    reported workspace must cover that plan too."""
+    st, h = _create(num_pages=8192, staged_from=16)
+    assert st == 0
+    pl = _plan(h, 2, 20, 32, 4096)
+    assert pl.kernel == 1 and pl.reduce == 0
+    ws = ctypes.c_size_t()
+    assert LIB.paged_attn_workspace_bytes(h, 2, 20, 32, 4096, ctypes.byref(ws)) == 0
+    st2, h2 = _create(num_pages=8192, staged_from=-1)      # the split plan itself
+    tree = _plan(h2, 2, 20, 32, 4096)
+    assert tree.kernel == 0 and tree.reduce == 1
+    need = ctypes.c_size_t()
+    assert LIB.paged_attn_workspace_bytes(h2, 2, 20, 32, 4096, ctypes.byref(need)) == 0
+    assert ws.value >= need.value > 0
+    LIB.paged_attn_destroy_pool(h)
+    LIB.paged_attn_destroy_pool(h2)

@@ -451,3 +451,16 @@ def test_timed_call_same_output_and_kernel_time(pa, kind):
     kern, call = k0.elapsed_ms(k1), c0.elapsed_ms(c1)
     say(f"    {kind}: kernel {kern * 1e3:.2f} us inside call {call * 1e3:.2f} us")
     assert 0 < kern <= call
+
+
+
+def test_tree_call_with_low_staged_from(pa):
+    """A pool whose staged_from (16) is below the tree size (20 nodes): the causal
+    plan of the shape is the chunked-prefill one, the tree call must still take
+    the split tree path with the workspace the library reports."""
+    n = 20
+    case = small_case("bf16", n, 32, 8, [3000, 900, 41], seed=321)
+    rng = np.random.default_rng(322)
+    case.tree_mask = np.stack([W.random_tree(rng, n)[1] for _ in range(case.batch)])
+    check(run_gpu(pa, case, label="tree, staged_from 16", staged_from=16), run_oracle(case),
+          "bf16", "tree staged_from=16")

@@ -264,6 +264,11 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
         if ((e = launch_staged(sa, d.kv_dtype == PA_FP8_E4M3, staged_tree, st, e0, e1)) != hipSuccess)
             return hip_fail(e, "staged kernel launch");
     } else {
+        // the partition kernel decodes blockIdx as (sequence, kv head, row chunk,
+        // partition): only its own plan may reach it
+        if (pl.kernel != 0 || pl.row_tiles < 1 || pl.row_tiles > kMaxRowTiles ||
+            (int64_t)pl.grid != (int64_t)batch * d.num_kv_heads * pl.row_chunks * pl.num_splits)
+            return fail(PA_ERR_INVALID_ARG, "internal: plan does not fit the partition kernel");
         const int pf = d.prefetch > 0 ? d.prefetch : default_prefetch(d.kv_dtype, pl.row_tiles);
         if ((e = launch_partition(a, d.kv_dtype, pl.row_tiles, pl.waves, pf, pl.grid, st, e0, e1)) !=
             hipSuccess)

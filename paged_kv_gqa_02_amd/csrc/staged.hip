@@ -64,6 +64,9 @@ constexpr float kNoMax = -1.0e30f;
 // draft-tree workgroups on a CU and the accumulators in VGPRs; deeper rings
 // measured no faster on MI355X.
 constexpr int kRing = 4;
+// key groups of the draft-tree kernel (8 waves, each pair of waves on one row
+// tile); chunked prefill uses one
+constexpr int kTreeKeyGroups = 2;
 constexpr float kRescaleSlack = 8.0f;
 
 // One pair of pages in LDS, in the pool's layouts: [K page 0][K page 1]
@@ -81,7 +84,10 @@ template <bool FP8, int WAVES> struct Layout {
 // fills 1 KiB.  base and lds are wave-uniform (scalar registers).  Issued as
 // inline assembly so that the compiler does not wait for it before every LDS
 // read; the kernel counts these loads itself (s_waitcnt vmcnt) and there are
-// no other global loads in its main loop.
+// no other global loads in its main loop.  NT: a non-temporal load, for pages
+// that no other workgroup reads again (draft trees: 5 % faster); chunked
+// prefill keeps the default policy, as its row blocks re-read pages through L2.
+template <bool NT>
 __device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t lds)
 {
     const uint64_t addr = reinterpret_cast<uint64_t>(src);
@@ -89,10 +95,16 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t l
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
     const uint64_t base = (uint64_t)lo | ((uint64_t)hi << 32);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(base), "s"(lds)
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     :
+                     : "v"(voff), "s"(base), "s"(lds)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :
+                     : "v"(voff), "s"(base), "s"(lds)
+                     : "memory");
 }
 
 template <int N>
@@ -112,7 +124,7 @@ __device__ __forceinline__ int vswz(int row) { return 2 * (row & 7); }
 // chunk l % 16, and fetches the chunk that the swizzle puts there.
 // ids[last] is the sequence's last page: a pair reaching past it repeats that
 // page (its tokens are masked and its V rows zeroed).
-template <bool FP8, int WAVES>
+template <bool FP8, int WAVES, bool NT>
 __device__ __forceinline__ void issue_pair(const StagedArgs& a, const int32_t* ids, int npairs,
                                            int last, int j, int kh, int wave, int lane,
                                            uint32_t stage_lds)
@@ -143,7 +155,7 @@ __device__ __forceinline__ void issue_pair(const StagedArgs& a, const int32_t* i
     }
 #pragma unroll
     for (int i = 0; i < Ly::kLoadsPerWave; ++i)
-        dma16(src[i], voff[i],
+        dma16<NT>(src[i], voff[i],
               __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (wave * Ly::kLoadsPerWave + i)));
 }
 
@@ -162,23 +174,32 @@ __device__ __forceinline__ u32x4 k_operand_fp8(const uint8_t* kp, int c, int l16
 // for at least two waves per SIMD caps a lane at 256 registers, so the MFMA
 // accumulators stay in VGPRs, where the rescale can reach them (in AGPRs they
 // would be copied out and back on every pair).
-template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP>
-__global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs a)
+//
+// KG key groups: the workgroup has WAVES * KG waves; waves w and w + WAVES
+// hold the same query rows (WAVES row waves) and walk alternate pairs of the
+// partition (key group k takes pairs KG j + k), each group copying its own
+// pairs; their online-softmax states merge in LDS at the end.  With one row
+// tile per wave (draft trees) this puts two waves on every SIMD, and twice the
+// copies in flight, without a second workgroup's entry cost.
+template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP, int KG>
+__global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(StagedArgs a)
 {
     using Ly = Layout<FP8, WAVES>;
     constexpr int kStages = STAGES;
-    constexpr int kThreads = WAVES * kWave;
+    constexpr int kThreads = WAVES * KG * kWave;
     constexpr int kRowsPerWave = 16 * TILES;
     constexpr int kRows = WAVES * kRowsPerWave;
+    constexpr int kStep = KG * Ly::kStage;         // LDS bytes of one step (KG pairs)
     static_assert((kStages - 2) * Ly::kLoadsPerWave <= 63, "vmcnt counts at most 63 loads");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * Ly::kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStep];
     constexpr int kIds = MAXP + 2;
     __shared__ __attribute__((aligned(8))) int32_t ids[kIds];
     __shared__ float scales[FP8 ? 2 * kIds : 1];   // k then v, per page of the block
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
-    const int wave = t / kWave;
+    const int wave = KG == 1 ? t / kWave : t / kWave % WAVES;   // row wave
+    const int kg = KG == 1 ? 0 : t / kWave / WAVES;             // key group
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
@@ -290,8 +311,7 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
     // Scores of pair jp for every tile, raw: K operands of both pages from LDS,
     // QK^T on the MFMAs.  The scale (and an E4M3 page's K scale) is folded into
     // the exponent later: p = exp2(s * f - m) with f > 0, so max(s * f) = f * max(s).
-    auto scores = [&](int jp, float (&sc)[TILES][8]) {
-        const uint8_t* st = lds + (jp % kStages) * Ly::kStage;
+    auto scores = [&](const uint8_t* st, float (&sc)[TILES][8]) {
         u32x4 kf[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -322,47 +342,59 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
         __builtin_amdgcn_s_setprio(0);
     };
 
+    // step j holds pairs KG j .. KG j + KG - 1, pair KG j + k in sub-stage k;
+    // key group k copies and computes pair KG j + k
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    const int nsteps = KG == 1 ? npairs : (npairs + KG - 1) / KG;
     if (npairs > 0) {
-        // prologue: pairs 0 .. kStages - 2 in flight (past the end: repeats)
+        // prologue: steps 0 .. kStages - 2 in flight (past the end: repeats)
 #pragma unroll
         for (int j = 0; j < kStages - 1; ++j)
-            issue_pair<FP8, WAVES>(a, ids, npairs, last, j, kh, wave, lane, lds0 + j * Ly::kStage);
+            issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * j + kg, kh, wave, lane,
+                                         lds0 + j * kStep + kg * Ly::kStage);
     }
 
-    for (int j = 0; j < npairs; ++j) {
-        // this wave's part of pair j has landed once at most the later pairs'
+    for (int j = 0; j < nsteps; ++j) {
+        // this wave's part of step j has landed once at most the later steps'
         // loads are outstanding; the barrier then covers every wave's part, and
-        // every wave is done with pair j - 1, whose stage is refilled next
+        // every wave is done with step j - 1, whose stage is refilled next
         wait_dma<(kStages - 2) * Ly::kLoadsPerWave>();
         __syncthreads();
-        issue_pair<FP8, WAVES>(a, ids, npairs, last, j + kStages - 1, kh, wave, lane,
-                               lds0 + ((j + kStages - 1) % kStages) * Ly::kStage);
+        issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * (j + kStages - 1) + kg, kh, wave,
+                                     lane, lds0 + ((j + kStages - 1) % kStages) * kStep +
+                                               kg * Ly::kStage);
 
-        uint8_t* st = lds + (j % kStages) * Ly::kStage;
-        const int base = 16 * pg0 + 32 * j;       // first token of the pair
-        const bool need_mask = base + 31 > wave_lim || base + 31 >= tok_end;
-        if (base + 31 >= L) {
-            // the pair holding the sequence end: V rows past it may hold NaN,
+        const int step_base = 16 * pg0 + 32 * KG * j;     // first token of the step
+        if (step_base + 32 * KG - 1 >= L) {
+            // the step holding the sequence end: V rows past it may hold NaN,
             // which a zero weight would still carry through the MFMA, so they
-            // are zeroed in LDS (once per workgroup, on this pair only)
+            // are zeroed in LDS (once per workgroup, on this step only)
             constexpr int kRowBytes = kHeadDim * Ly::kElem;
-            for (int e = t; e < 32 * kRowBytes / 16; e += WAVES * kWave) {
-                const int tok = e / (kRowBytes / 16);
-                if (base + tok >= L)
-                    *reinterpret_cast<u32x4*>(st + (2 + tok / 16) * Ly::kPageBytes +
-                                              (tok % 16) * kRowBytes + 16 * (e % (kRowBytes / 16))) =
-                        u32x4{0u, 0u, 0u, 0u};
+            constexpr int kChunks = 32 * kRowBytes / 16;   // 16-byte pieces of a pair's V rows
+            for (int e = t; e < KG * kChunks; e += kThreads) {
+                const int sub = KG == 1 ? 0 : e / kChunks;
+                const int ep = KG == 1 ? e : e % kChunks;
+                const int tok = ep / (kRowBytes / 16);
+                if (step_base + 32 * sub + tok >= L)
+                    *reinterpret_cast<u32x4*>(lds + (j % kStages) * kStep + sub * Ly::kStage +
+                                              (2 + tok / 16) * Ly::kPageBytes + (tok % 16) * kRowBytes +
+                                              16 * (ep % (kRowBytes / 16))) = u32x4{0u, 0u, 0u, 0u};
             }
             __syncthreads();
         }
+        const int jp = KG * j + kg;               // this wave's pair
+        if constexpr (KG > 1)
+            if (jp >= npairs) continue;           // (a key group past the end idles)
+        uint8_t* st = lds + (j % kStages) * kStep + kg * Ly::kStage;
+        const int base = 16 * pg0 + 32 * jp;      // first token of the pair
+        const bool need_mask = base + 31 > wave_lim || base + 31 >= tok_end;
         float sc[TILES][8];
-        scores(j, sc);
+        scores(st, sc);
         float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
         if constexpr (FP8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int pg = min(2 * j + h, last);
+                const int pg = min(2 * jp + h, last);
                 ks[h] = scales[pg];
                 vs[h] = scales[kIds + pg];
             }
@@ -478,6 +510,55 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
     }
     // no copy may still be writing this workgroup's LDS when it exits
     wait_dma<0>();
+    if constexpr (KG > 1) {
+        // key groups 1 .. KG - 1 hand their (max, sum, accumulator) to group 0
+        // through the ring, lane by lane; group 0 merges them with weights
+        // 2^(m_k - max) and writes the result
+        constexpr int kSlot = TILES * 34;          // floats per lane: acc, m, l of each tile
+        float* xs = reinterpret_cast<float*>(lds);
+        static_assert((KG - 1) * WAVES * kWave * kSlot * 4 <= kStages * kStep, "merge fits the ring");
+        __syncthreads();                           // every wave is done with the ring
+        if (kg > 0) {
+            float* my = xs + ((size_t)((kg - 1) * WAVES + wave) * kWave + lane) * kSlot;
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) my[tt * 34 + 4 * db + v] = acc[tt][db][v];
+                my[tt * 34 + 32] = m[tt];
+                my[tt * 34 + 33] = FP8 ? l[tt] : lsum[tt][0];
+            }
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int tt = 0; tt < TILES; ++tt) {
+            float mm = m[tt];
+#pragma unroll
+            for (int k = 1; k < KG; ++k)
+                mm = fmaxf(mm, xs[((size_t)((k - 1) * WAVES + wave) * kWave + lane) * kSlot + tt * 34 + 32]);
+            const float s0 = fast_exp2(m[tt] - mm);
+            float lt = (FP8 ? l[tt] : lsum[tt][0]) * s0;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) acc[tt][db] *= s0;
+#pragma unroll
+            for (int k = 1; k < KG; ++k) {
+                const float* o = xs + ((size_t)((k - 1) * WAVES + wave) * kWave + lane) * kSlot + tt * 34;
+                const float sk = fast_exp2(o[32] - mm);
+                lt += o[33] * sk;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[tt][db][v] += o[4 * db + v] * sk;
+            }
+            m[tt] = mm;
+            if constexpr (FP8)
+                l[tt] = lt;
+            else
+                lsum[tt][0] = lt;
+        }
+    }
 
     // epilogue: lane holds O[row l16][32 g + 8 v + db] (E4M3 pools) or
     // O[row l16][16 db + 4 g + v] (bf16 pools) of each tile; the final output
@@ -544,11 +625,11 @@ __global__ __launch_bounds__(WAVES * kWave, 2) void paged_attn_staged(StagedArgs
 
 namespace {
 
-template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP>
+template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP, int KG>
 hipError_t launch(const StagedArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    hipExtLaunchKernelGGL((paged_attn_staged<FP8, WAVES, TILES, TREE, STAGES, MAXP>), grid,
-                          dim3(WAVES * kWave), 0, st, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((paged_attn_staged<FP8, WAVES, TILES, TREE, STAGES, MAXP, KG>), grid,
+                          dim3(WAVES * KG * kWave), 0, st, e0, e1, 0, a);
     return hipGetLastError();
 }
 
@@ -559,8 +640,10 @@ hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t s
 {
     const dim3 grid((unsigned)((int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits));
     if (tree)
-        return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st, e0, e1)
-                   : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages>(a, grid, st, e0, e1);
-    return fp8 ? launch<true, 4, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1)
-               : launch<false, 4, 2, false, kRing, kStagedMaxPages>(a, grid, st, e0, e1);
+        return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages, kTreeKeyGroups>(a, grid, st,
+                                                                                        e0, e1)
+                   : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages, kTreeKeyGroups>(a, grid, st,
+                                                                                         e0, e1);
+    return fp8 ? launch<true, 4, 2, false, kRing, kStagedMaxPages, 1>(a, grid, st, e0, e1)
+               : launch<false, 4, 2, false, kRing, kStagedMaxPages, 1>(a, grid, st, e0, e1);
 }

@@ -464,3 +464,57 @@ def test_tree_call_with_low_staged_from(pa):
     case.tree_mask = np.stack([W.random_tree(rng, n)[1] for _ in range(case.batch)])
     check(run_gpu(pa, case, label="tree, staged_from 16", staged_from=16), run_oracle(case),
           "bf16", "tree staged_from=16")
+
+
+def _perturb_token(case, b, t, rng):
+    """Give token t of sequence b new K and V rows (every kv head), in place."""
+    page = int(case.block_table[b, t // W.PAGE_SIZE])
+    slot = t % W.PAGE_SIZE
+    for kh in range(case.num_kv_heads):
+        k = rng.standard_normal(case.head_dim).astype(np.float32) * 3
+        v = rng.standard_normal(case.head_dim).astype(np.float32) * 3
+        if case.kv_dtype == "bf16":
+            k, v = W.bf16_bits(k), W.bf16_bits(v)
+        W.set_k_token(case.k_pool, page, kh, slot, k)
+        case.v_pool[page, kh, slot, :] = v
+
+
+@pytest.mark.parametrize("kind", ["verify", "prefill", "tree"])
+def test_causality_under_perturbation(pa, kind):
+    """New K/V for token j leave every row that does not see j bitwise unchanged
+    (and change the rows that do): the causal limit, the chunked-prefill kernel's
+    limit and the tree's ancestor masks, each on its own kernel."""
+    rng = np.random.default_rng(880)
+    n = {"verify": 5, "prefill": 160, "tree": 16}[kind]
+    case = small_case("bf16", n, 32, 8, [700, n + 3, 1300], seed=881)
+    if kind == "tree":
+        case.tree_mask = np.stack([W.random_tree(rng, n)[1] for _ in range(case.batch)])
+    before = run_gpu(pa, case, label=f"{kind} before")
+    j = {"verify": 3, "prefill": 100, "tree": 9}[kind]
+    for b in range(case.batch):
+        _perturb_token(case, b, int(case.seq_lens[b]) - n + j, rng)
+    after = run_gpu(pa, case, label=f"{kind} after")
+    for b in range(case.batch):
+        for i in range(n):
+            sees = (int(case.tree_mask[b, i]) >> j) & 1 if kind == "tree" else i >= j
+            same = np.array_equal(before[b, i], after[b, i])
+            assert same != bool(sees), f"{kind}: b={b} row {i} {'changed' if not same else 'unchanged'}"
+
+
+@pytest.mark.parametrize("kv,n", [("bf16", 1), ("bf16", 5), ("f32", 5), ("bf16", 16)])
+def test_gqa_mapping_with_constant_values(pa, kv, n):
+    """V of kv head k equal to k everywhere: query head h must return h // G, whatever
+    the keys and queries (the head grouping, on the decode, verify and tree paths)."""
+    hq, hkv = 32, 4
+    case = small_case(kv, n, hq, hkv, [300, 57, 1000], seed=890)
+    for kh in range(hkv):
+        val = np.full(case.v_pool[:, kh].shape, float(kh), dtype=np.float32)
+        case.v_pool[:, kh] = W.bf16_bits(val) if kv == "bf16" else val
+    if n == 16:
+        rng = np.random.default_rng(891)
+        case.tree_mask = np.stack([W.random_tree(rng, n)[1] for _ in range(case.batch)])
+    out = run_gpu(pa, case, label="constant V")
+    want = (np.arange(hq) // (hq // hkv)).astype(np.float64)
+    err = float(np.abs(out - want[None, None, :, None]).max())
+    say(f"    GQA mapping {kv} n={n}: max_abs={err:.3e}")
+    assert err <= (1e-5 if kv == "f32" else 1e-6)

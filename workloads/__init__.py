@@ -377,12 +377,12 @@ def ragged_lengths(rng: np.random.Generator, batch: int = 240) -> np.ndarray:
     return (prompt + gen).astype(np.int32)
 
 
-WORKLOADS = ("tiny", "decode8b", "ragged", "verify", "fp8long", "tree", "prefill")
+WORKLOADS = ("tiny", "decode8b", "ragged", "verify", "fp8long", "tree", "prefill", "verify_decode")
 
 
 def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] = None,
              seed: Optional[int] = None, poison: bool = True) -> Case:
-    """The five named workloads; dtype overrides give same-shape structural runs.
+    """The named workloads; dtype overrides give same-shape structural runs.
 
     tiny      B1, 8/2 heads, ctx 64, 16-page pool (4 pages used), fp32
     decode8b  B64, 32/8 heads, ctx 2048, 8192-page pool, bf16
@@ -393,6 +393,8 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
               4096-token context (draft-tree verification), bf16
     prefill   B4, 32/8 heads, one 512-token prefill chunk per sequence after 1536, 1024,
               512 and 0 earlier tokens (a 2048-token prompt in four chunks), bf16
+    verify_decode  verify's shape and seed with one query row per sequence (decode at
+              the same context: the verify / decode time comparison)
     """
     idx = WORKLOADS.index(name)
     s = BASE_SEED + idx if seed is None else seed
@@ -417,6 +419,14 @@ def workload(name: str, kv_dtype: Optional[str] = None, q_dtype: Optional[str] =
     if name == "verify":
         kv, qd = kv_dtype or "bf16", q_dtype or "bf16"
         return make_case(name, batch=8, q_per_seq=5, num_q_heads=32, num_kv_heads=8,
+                         seq_lens=[4096 + 5] * 8, kv_dtype=kv, q_dtype=qd, seed=s,
+                         poison=poison)
+    if name == "verify_decode":
+        # the verify workload's pool and lengths with one query row per sequence:
+        # decode at the same context, for the verify / decode time ratio
+        kv, qd = kv_dtype or "bf16", q_dtype or "bf16"
+        s = BASE_SEED + WORKLOADS.index("verify") if seed is None else seed
+        return make_case(name, batch=8, q_per_seq=1, num_q_heads=32, num_kv_heads=8,
                          seq_lens=[4096 + 5] * 8, kv_dtype=kv, q_dtype=qd, seed=s,
                          poison=poison)
     if name == "fp8long":

@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode8b", choices=W.WORKLOADS)
+    ap.add_argument("--kv-dtype", default=None, choices=("bf16", "fp8", "f32"),
+                    help="K/V pool dtype in place of the workload's own (same shape)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0, help="pool knob: waves per workgroup")
     ap.add_argument("--prefetch", type=int, default=0, help="pool knob: pages in flight per wave")
@@ -360,7 +362,7 @@ def main():
         return
 
     log(f"generating {args.workload}")
-    case = W.workload(args.workload)
+    case = W.workload(args.workload, kv_dtype=args.kv_dtype)
     dev = to_device(case)
     pool = pa.paged_attn_create_pool(dev.k, dev.v, dev.k_scale, dev.v_scale,
                                      args.partition_pages, args.waves, args.prefetch,

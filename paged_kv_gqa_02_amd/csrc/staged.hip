@@ -15,10 +15,10 @@
 // Design (gfx950, wave64):
 //  * a workgroup takes WAVES * TILES * 16 query rows of one (sequence, kv head)
 //    and one context partition; each wave owns TILES 16-row MFMA tiles.
-//    Chunked prefill uses 4 waves x 2 tiles (128 rows; two workgroups per CU,
-//    so that one wave's softmax arithmetic overlaps another's MFMAs, and the
-//    unequal row blocks of sequences at different chunk stages share CUs),
-//    draft trees 4 waves x 1 tile (64 rows, few registers per wave);
+//    Chunked prefill uses 4 waves x 2 tiles (128 rows), draft trees 4 waves
+//    x 1 tile (64 rows, few registers per wave), both with two key groups
+//    (below): a row block's chain of pairs, which sets its workgroup's time,
+//    is cut in two;
 //  * the keys are walked in steps of two pages (32 tokens).  The workgroup
 //    copies each pair once into a ring of four LDS stages with direct
 //    global-to-LDS loads, three pairs ahead of the one being consumed, so no
@@ -46,6 +46,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 #include "cdna4.h"
@@ -64,9 +65,10 @@ constexpr float kNoMax = -1.0e30f;
 // draft-tree workgroups on a CU and the accumulators in VGPRs; deeper rings
 // measured no faster on MI355X.
 constexpr int kRing = 4;
-// key groups of the draft-tree kernel (8 waves, each pair of waves on one row
-// tile); chunked prefill uses one
+// key groups: the draft-tree kernel (8 waves, each pair of waves on one row
+// tile) and the chunked-prefill kernel (8 waves, each pair on two row tiles)
 constexpr int kTreeKeyGroups = 2;
+constexpr int kPrefillKeyGroups = 2;
 constexpr float kRescaleSlack = 8.0f;
 
 // One pair of pages in LDS, in the pool's layouts: [K page 0][K page 1]
@@ -178,9 +180,10 @@ __device__ __forceinline__ u32x4 k_operand_fp8(const uint8_t* kp, int c, int l16
 // KG key groups: the workgroup has WAVES * KG waves; waves w and w + WAVES
 // hold the same query rows (WAVES row waves) and walk alternate pairs of the
 // partition (key group k takes pairs KG j + k), each group copying its own
-// pairs; their online-softmax states merge in LDS at the end.  With one row
-// tile per wave (draft trees) this puts two waves on every SIMD, and twice the
-// copies in flight, without a second workgroup's entry cost.
+// pairs; their online-softmax states merge in LDS at the end.  This puts two
+// waves on every SIMD, and twice the copies in flight, without a second
+// workgroup's entry cost; for chunked prefill it halves the chain of pairs of
+// the heaviest row blocks, which set the kernel's time.
 template <bool FP8, int WAVES, int TILES, bool TREE, int STAGES, int MAXP, int KG>
 __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(StagedArgs a)
 {
@@ -203,21 +206,53 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
-    // blockIdx -> (split, sequence and kv head, row block): heavy row blocks
-    // first; the row blocks of one (sequence, kv head, split) share blockIdx
-    // mod (B * Hkv * splits), hence one XCD and its L2 when that is a multiple of 8
-    const int sp = blockIdx.x % a.num_splits;
-    const int rest = blockIdx.x / a.num_splits;
-    const int bh_count = a.batch * a.hkv;
-    const int bh = rest % bh_count;
-    const int rb = a.row_blocks - 1 - rest / bh_count;
-    const int kh = bh % a.hkv;
-    const int b = bh / a.hkv;
+    int sp, b, kh, rb, seq_len;
+    {
+        sp = blockIdx.x % a.num_splits;
+        const int rest = blockIdx.x / a.num_splits;
+        if constexpr (TREE) {
+            // (sequence, kv head) pairs in blockIdx order, one row block each
+            const int bh_count = a.batch * a.hkv;
+            const int bh = rest % bh_count;
+            rb = a.row_blocks - 1 - rest / bh_count;
+            kh = bh % a.hkv;
+            b = bh / a.hkv;
+            seq_len = a.seq_lens[b];
+        } else {
+            // Causal row blocks differ in work: a block of a sequence with c
+            // earlier tokens walks c / 32 + (its index + 1) * (tokens per block) / 32
+            // pairs, and a workgroup's time follows its pair count.  blockIdx
+            // takes the slots (sequence rank, row block) heaviest first,
+            // sequences ranked by length (longest first), so that the
+            // dispatcher hands the lightest work to the CUs that finish first
+            // (one workgroup per CU).  The kv head is blockIdx's fastest
+            // index: the row blocks of one (sequence, kv head) share blockIdx
+            // mod Hkv, hence one XCD and its L2 when Hkv is a multiple of 8.
+            kh = rest % a.hkv;
+            const int q = rest / a.hkv;
+            const int rank = q / a.row_blocks;
+            rb = a.row_blocks - 1 - (q - rank * a.row_blocks);
+            if (a.batch <= kWave) {
+                // rank sequences by length in one wave: lane u holds length u
+                const int mine = lane < a.batch ? a.seq_lens[lane] : INT_MIN;
+                int r = 0;
+                for (int u = 0; u < a.batch; ++u) {
+                    const int lu = __builtin_amdgcn_readlane(mine, u);
+                    r += (lu > mine || (lu == mine && u < lane)) ? 1 : 0;
+                }
+                const uint64_t hit = __ballot(lane < a.batch && r == rank);
+                b = hit ? (int)__builtin_ctzll(hit) : rank;   // (ranks are a permutation)
+                seq_len = __builtin_amdgcn_readlane(mine, b);
+            } else {
+                b = rank;                          // many sequences: index order
+                seq_len = a.seq_lens[b];
+            }
+        }
+    }
 
     // Every load of the prologue is issued before the first one is waited for:
-    // the sequence length, this partition's block-table entries, the query rows
-    // and their tree masks (only the length decides what is used of them).
-    const int seq_len = a.seq_lens[b];
+    // this partition's block-table entries, the query rows and their tree masks
+    // (only the sequence length decides what is used of them).
     const int pg0 = sp * a.part_pages;
     const int part = min(a.part_pages, MAXP);     // a larger partition is cut short
     const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
@@ -512,52 +547,54 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
     wait_dma<0>();
     if constexpr (KG > 1) {
         // key groups 1 .. KG - 1 hand their (max, sum, accumulator) to group 0
-        // through the ring, lane by lane; group 0 merges them with weights
-        // 2^(m_k - max) and writes the result
-        constexpr int kSlot = TILES * 34;          // floats per lane: acc, m, l of each tile
+        // through the ring, one tile at a time, value x of a lane at
+        // xs[x * kLanes + lane id] (consecutive lanes, consecutive words);
+        // group 0 merges them with weights 2^(m_k - max) and writes the result
+        constexpr int kLanes = (KG - 1) * WAVES * kWave;
+        constexpr int kVals = 34;                  // acc (32), m, l of one tile
         float* xs = reinterpret_cast<float*>(lds);
-        static_assert((KG - 1) * WAVES * kWave * kSlot * 4 <= kStages * kStep, "merge fits the ring");
+        static_assert(kLanes * kVals * 4 <= kStages * kStep, "merge fits the ring");
         __syncthreads();                           // every wave is done with the ring
-        if (kg > 0) {
-            float* my = xs + ((size_t)((kg - 1) * WAVES + wave) * kWave + lane) * kSlot;
-#pragma unroll
-            for (int tt = 0; tt < TILES; ++tt) {
-#pragma unroll
-                for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) my[tt * 34 + 4 * db + v] = acc[tt][db][v];
-                my[tt * 34 + 32] = m[tt];
-                my[tt * 34 + 33] = FP8 ? l[tt] : lsum[tt][0];
-            }
-        }
-        __syncthreads();
-        if (kg > 0) return;
 #pragma unroll
         for (int tt = 0; tt < TILES; ++tt) {
-            float mm = m[tt];
-#pragma unroll
-            for (int k = 1; k < KG; ++k)
-                mm = fmaxf(mm, xs[((size_t)((k - 1) * WAVES + wave) * kWave + lane) * kSlot + tt * 34 + 32]);
-            const float s0 = fast_exp2(m[tt] - mm);
-            float lt = (FP8 ? l[tt] : lsum[tt][0]) * s0;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) acc[tt][db] *= s0;
-#pragma unroll
-            for (int k = 1; k < KG; ++k) {
-                const float* o = xs + ((size_t)((k - 1) * WAVES + wave) * kWave + lane) * kSlot + tt * 34;
-                const float sk = fast_exp2(o[32] - mm);
-                lt += o[33] * sk;
+            if (kg > 0) {
+                float* my = xs + ((kg - 1) * WAVES + wave) * kWave + lane;
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[tt][db][v] += o[4 * db + v] * sk;
+                    for (int v = 0; v < 4; ++v) my[(4 * db + v) * kLanes] = acc[tt][db][v];
+                my[32 * kLanes] = m[tt];
+                my[33 * kLanes] = FP8 ? l[tt] : lsum[tt][0];
             }
-            m[tt] = mm;
-            if constexpr (FP8)
-                l[tt] = lt;
-            else
-                lsum[tt][0] = lt;
+            __syncthreads();
+            if (kg == 0) {
+                float mm = m[tt];
+#pragma unroll
+                for (int k = 1; k < KG; ++k)
+                    mm = fmaxf(mm, xs[32 * kLanes + ((k - 1) * WAVES + wave) * kWave + lane]);
+                const float s0 = fast_exp2(m[tt] - mm);
+                float lt = (FP8 ? l[tt] : lsum[tt][0]) * s0;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) acc[tt][db] *= s0;
+#pragma unroll
+                for (int k = 1; k < KG; ++k) {
+                    const float* o = xs + ((k - 1) * WAVES + wave) * kWave + lane;
+                    const float sk = fast_exp2(o[32 * kLanes] - mm);
+                    lt += o[33 * kLanes] * sk;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[tt][db][v] += o[(4 * db + v) * kLanes] * sk;
+                }
+                m[tt] = mm;
+                if constexpr (FP8)
+                    l[tt] = lt;
+                else
+                    lsum[tt][0] = lt;
+            }
+            if (tt + 1 < TILES) __syncthreads();   // group 0 is done reading the slots
         }
+        if (kg > 0) return;
     }
 
     // epilogue: lane holds O[row l16][32 g + 8 v + db] (E4M3 pools) or
@@ -644,6 +681,8 @@ hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t s
                                                                                         e0, e1)
                    : launch<false, 4, 1, true, kRing, kStagedTreeMaxPages, kTreeKeyGroups>(a, grid, st,
                                                                                          e0, e1);
-    return fp8 ? launch<true, 4, 2, false, kRing, kStagedMaxPages, 1>(a, grid, st, e0, e1)
-               : launch<false, 4, 2, false, kRing, kStagedMaxPages, 1>(a, grid, st, e0, e1);
+    return fp8 ? launch<true, 4, 2, false, kRing, kStagedMaxPages, kPrefillKeyGroups>(a, grid, st,
+                                                                                    e0, e1)
+               : launch<false, 4, 2, false, kRing, kStagedMaxPages, kPrefillKeyGroups>(a, grid, st,
+                                                                                     e0, e1);
 }

@@ -115,6 +115,9 @@ __device__ __forceinline__ void wait_dma()
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// a wave-uniform value, marked as such for the compiler
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // bf16 V rows in LDS: 16-byte chunk c of row r is stored at chunk c ^ vswz(r),
 // so that the eight rows one transposing read touches fall in distinct banks.
 __device__ __forceinline__ int vswz(int row) { return 2 * (row & 7); }
@@ -133,13 +136,14 @@ __device__ __forceinline__ void issue_pair(const StagedArgs& a, const int32_t* i
 {
     using Ly = Layout<FP8, WAVES>;
     constexpr int kPieces = Ly::kPageBytes / 1024;       // per slab
-    const int jj = min(j, npairs - 1);                   // past the end: a harmless repeat
+    const int jj = uni(min(j, npairs - 1));              // past the end: a harmless repeat
     // both page ids of the pair in one LDS read, before any copy is issued (each
     // copy is a compiler barrier for memory, which would re-read them); page ids
     // are wave-uniform, so slab addresses are formed on the scalar unit
-    const int2 pp = *reinterpret_cast<const int2*>(ids + 2 * jj);
-    const int p0 = __builtin_amdgcn_readfirstlane(pp.x);
-    const int page[2] = {p0, 2 * jj + 1 <= last ? __builtin_amdgcn_readfirstlane(pp.y) : p0};
+    const uint64_t pp = *reinterpret_cast<const uint64_t*>(ids + 2 * jj);
+    const int p0 = uni((int)(uint32_t)pp);
+    const int p1 = uni((int)(uint32_t)(pp >> 32));
+    const int page[2] = {p0, 2 * jj + 1 <= last ? p1 : p0};
     const uint8_t* src[Ly::kLoadsPerWave];
     uint32_t voff[Ly::kLoadsPerWave];
 #pragma unroll
@@ -201,8 +205,11 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
-    const int wave = KG == 1 ? t / kWave : t / kWave % WAVES;   // row wave
-    const int kg = KG == 1 ? 0 : t / kWave / WAVES;             // key group
+    // (read through readfirstlane, so that the compiler knows them to be
+    // wave-uniform and keeps what derives from them in scalar registers)
+    const int wave_id = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int wave = KG == 1 ? wave_id : wave_id % WAVES;       // row wave
+    const int kg = KG == 1 ? 0 : wave_id / WAVES;               // key group
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
@@ -248,6 +255,10 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
                 seq_len = a.seq_lens[b];
             }
         }
+        sp = uni(sp);
+        b = uni(b);
+        kh = uni(kh);
+        rb = uni(rb);
     }
 
     // Every load of the prologue is issued before the first one is waited for:
@@ -257,12 +268,12 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
     const int part = min(a.part_pages, MAXP);     // a larger partition is cut short
     const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
     constexpr int kIdLoads = (kIds + kThreads - 1) / kThreads;
+    // (unconditional loads from clamped, in-bounds addresses: under a lane
+    // mask the compiler would wait for each load before issuing the next)
     int idv[kIdLoads];
 #pragma unroll
-    for (int k = 0; k < kIdLoads; ++k) {
-        const int p = t + k * kThreads;
-        idv[k] = p <= part ? bt_row[min(pg0 + p, a.max_pages - 1)] : 0;
-    }
+    for (int k = 0; k < kIdLoads; ++k)
+        idv[k] = bt_row[min(pg0 + min(t + k * kThreads, part), a.max_pages - 1)];
     const int row0 = rb * kRows;
     const int wrow0 = row0 + wave * kRowsPerWave;
     // query rows of this wave (MFMA B-operand layout: lane holds row l16 of a tile)
@@ -290,17 +301,20 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
 
     // lengths clamped to what the block table describes: arrays that break the
     // contract give wrong numbers, never a stray access
-    const int L = max(min(seq_len, a.max_pages * kPage), 1);
+    // (the values below are wave-uniform; readfirstlane keeps them, and the
+    // loop control and page addresses derived from them, in scalar registers
+    // where a division or a loaded value would otherwise leave them in VGPRs)
+    const int L = uni(max(min(seq_len, a.max_pages * kPage), 1));
     const int seq_pages = (L + kPage - 1) / kPage;
-    const int nsplit_b = min((seq_pages + a.part_pages - 1) / a.part_pages, a.num_splits);
+    const int nsplit_b = uni(min((seq_pages + a.part_pages - 1) / a.part_pages, a.num_splits));
     if (sp >= nsplit_b) return;                   // this sequence has fewer partitions
     const int last_row = min(row0 + kRows, a.rows) - 1;
     const int first_limit = L - a.n;              // row 0 sees tokens 0 .. L - n (causal)
     // keys the block needs: up to the causal limit of its last row, or all (tree)
-    const int key_end = TREE ? L : max(min(L, first_limit + last_row / a.group + 1), 1);
-    const int pg_end = min(pg0 + part, (key_end + kPage - 1) / kPage);
-    const int npairs = max(pg_end - pg0 + 1, 0) / 2;
-    const int last = seq_pages - 1 - pg0;         // the sequence's last page, partition-relative
+    const int key_end = TREE ? L : uni(max(min(L, first_limit + last_row / a.group + 1), 1));
+    const int pg_end = uni(min(pg0 + part, (key_end + kPage - 1) / kPage));
+    const int npairs = uni(max(pg_end - pg0 + 1, 0) / 2);
+    const int last = uni(seq_pages - 1 - pg0);    // the sequence's last page, partition-relative
     // the last pair of a partition with an odd page count reaches one page
     // into the next partition: keys from here on are masked like dead ones
     const int tok_end = min(L, kPage * pg_end);
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
         lim[tt] = qi[tt] >= 0 ? first_limit + qi[tt] : L - 1;   // padding rows see every live key
     // the pairs that need masks: those past the smallest causal limit among
     // this wave's rows, or reaching the tree tokens
-    const int wave_lim = TREE ? first_limit - 1 : first_limit + min(wrow0, a.rows - 1) / a.group;
+    const int wave_lim = TREE ? first_limit - 1 : uni(first_limit + min(wrow0, a.rows - 1) / a.group);
 
     // page ids (and E4M3 scales) of the partition, clamped to the pool
 #pragma unroll

@@ -37,6 +37,10 @@ __device__ __forceinline__ float bf16_float(uint32_t bits16)
     return __uint_as_float(bits16 << 16);
 }
 
+// a wave-uniform value, marked as such for the compiler (readfirstlane), so
+// that what derives from it is computed on the scalar unit
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float fast_exp2(float x)
 {
     return __builtin_amdgcn_exp2f(x);

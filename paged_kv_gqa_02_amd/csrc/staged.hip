@@ -115,8 +115,20 @@ __device__ __forceinline__ void wait_dma()
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// a wave-uniform value, marked as such for the compiler
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Waits until at most `ahead` (<= N, wave-uniform) later steps of L loads each
+// are outstanding.
+template <int N, int L>
+__device__ __forceinline__ void wait_steps(int ahead)
+{
+    if constexpr (N == 0) {
+        wait_dma<0>();
+    } else {
+        if (ahead >= N)
+            wait_dma<N * L>();
+        else
+            wait_steps<N - 1, L>(ahead);
+    }
+}
 
 // bf16 V rows in LDS: 16-byte chunk c of row r is stored at chunk c ^ vswz(r),
 // so that the eight rows one transposing read touches fall in distinct banks.
@@ -395,23 +407,25 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
     // key group k copies and computes pair KG j + k
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
     const int nsteps = KG == 1 ? npairs : (npairs + KG - 1) / KG;
-    if (npairs > 0) {
-        // prologue: steps 0 .. kStages - 2 in flight (past the end: repeats)
+    // prologue: steps 0 .. kStages - 2 in flight.  No step past the last is
+    // copied, so the loads outstanding after step j are those of the
+    // min(kStages - 2, nsteps - 1 - j) steps that follow it.
 #pragma unroll
-        for (int j = 0; j < kStages - 1; ++j)
+    for (int j = 0; j < kStages - 1; ++j)
+        if (j < nsteps)
             issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * j + kg, kh, wave, lane,
                                          lds0 + j * kStep + kg * Ly::kStage);
-    }
 
     for (int j = 0; j < nsteps; ++j) {
         // this wave's part of step j has landed once at most the later steps'
         // loads are outstanding; the barrier then covers every wave's part, and
         // every wave is done with step j - 1, whose stage is refilled next
-        wait_dma<(kStages - 2) * Ly::kLoadsPerWave>();
+        wait_steps<kStages - 2, Ly::kLoadsPerWave>(min(kStages - 2, nsteps - 1 - j));
         __syncthreads();
-        issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * (j + kStages - 1) + kg, kh, wave,
-                                     lane, lds0 + ((j + kStages - 1) % kStages) * kStep +
-                                               kg * Ly::kStage);
+        if (j + kStages - 1 < nsteps)
+            issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * (j + kStages - 1) + kg, kh,
+                                         wave, lane, lds0 + ((j + kStages - 1) % kStages) * kStep +
+                                                         kg * Ly::kStage);
 
         const int step_base = 16 * pg0 + 32 * KG * j;     // first token of the step
         if (step_base + 32 * KG - 1 >= L) {

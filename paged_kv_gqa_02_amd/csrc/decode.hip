@@ -332,20 +332,17 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     __shared__ float sm_fin[RT][2];
 
     const int lane = threadIdx.x & (kWave - 1);
-    // Wave-uniform values go through readfirstlane (uni), so that the compiler
-    // keeps them, and the loop control and addresses derived from them, in
-    // scalar registers (a division or a loaded value would leave them in VGPRs).
-    const int wave = uni(threadIdx.x / kWave);
+    const int wave = threadIdx.x / kWave;
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
     int unit = blockIdx.x;
-    const int split = uni(unit % a.num_splits);
+    const int split = unit % a.num_splits;
     unit /= a.num_splits;
-    const int rc = uni(unit % a.row_chunks);
+    const int rc = unit % a.row_chunks;
     unit /= a.row_chunks;
-    const int kh = uni(unit % a.hkv);
-    const int b = uni(unit / a.hkv);
+    const int kh = unit % a.hkv;
+    const int b = unit / a.hkv;
 
     // Block-table ids and query rows do not depend on the sequence length,
     // so they are requested together with it: the first page loads then wait
@@ -385,9 +382,9 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     // lengths are clamped to what the block table can describe, and page ids
     // to the pool, so that arrays breaking the contract give wrong numbers
     // but never an access outside the caller's buffers
-    const int L = uni(min(a.seq_lens[b], a.max_pages * kPage));
+    const int L = min(a.seq_lens[b], a.max_pages * kPage);
     const int npages = (L + kPage - 1) / kPage;
-    const int nsplit_b = uni(min((npages + a.part_pages - 1) / a.part_pages, a.num_splits));
+    const int nsplit_b = min((npages + a.part_pages - 1) / a.part_pages, a.num_splits);
     if (split >= nsplit_b) return;
     const int pg1 = min(pg0 + a.part_pages, npages);
     const int rows_here = min(RT, a.rows - row0);
@@ -412,7 +409,7 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     }
 
     // this wave's pages: pg0 + wave + j * W, j < nj (nj <= 64 by construction)
-    const int nj = uni((pg1 - pg0 - wave + W - 1) / W);
+    const int nj = (pg1 - pg0 - wave + W - 1) / W;
     const int my_id = (lane < nj) ? min(max(raw_id, 0), a.num_pages - 1) : 0;
 
     auto consume = [&](Page<KV>& pg, int j) {

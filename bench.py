@@ -14,6 +14,10 @@ every token of every sequence, fp8 scales, Q, O) / mean call time, the call
 bracketed by two HIP events on its stream.  `roofline.achieved` divides the
 same bytes by the attention kernel's own execution time, from events the
 library attaches to that kernel's dispatch (paged_attn_verify_timed).
+`copy_gbs` is the box's own device-copy bandwidth (bytes read + written by a
+512 MiB copy, timed the same way), and `pct_of_copy` / `roofline.frac_of_copy`
+the call's and the kernel's rates against it: a second denominator next to
+the 8 TB/s data-sheet peak.
 
 `--op append` instead times paged_attn_append_kv, the step before attention:
 the n_new newest tokens of every sequence of the workload (default: its query
@@ -330,6 +334,28 @@ def copy_calibration(torch):
                       "launches": 10}), flush=True)
 
 
+def measure_copy_gbs(torch, stream):
+    """The box's device-copy bandwidth, (bytes read + bytes written) / time, over
+    ten 512 MiB copies on `stream` bracketed by HIP events: a secondary
+    denominator for the HBM-bound lines, next to the 8 TB/s data-sheet peak."""
+    n = 512 << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            y.copy_(x)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            y.copy_(x)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -470,6 +496,11 @@ def main():
         result["roofline"].update({"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                                    "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                                    "hbm_gbs": round(achieved, 1)})
+    copy_gbs = measure_copy_gbs(torch, stream)
+    result["copy_gbs"] = round(copy_gbs, 1)
+    if not mfma_bound:
+        result["pct_of_copy"] = round(100 * gbs / copy_gbs, 2)
+        result["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(case, args.cpu_reps)

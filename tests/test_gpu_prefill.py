@@ -67,6 +67,24 @@ def test_prefill_kernel_edge_shapes(pa, kv, n, heads, lens):
     check(run(pa, case, "prefill"), run_oracle(case), kv, f"prefill edge n={n} {heads} {kv}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_sequences_ranked_by_length(pa, kv):
+    # the kernel orders row blocks by the sequences' lengths (longest first, ties
+    # by index): unsorted lengths with a tie and a first chunk of its own
+    n = 128
+    case = small_case(kv, n, 8, 2, [n + 100, n + 700, n, n + 700, n + 333], seed=940)
+    check(run(pa, case, "prefill"), run_oracle(case), kv, f"prefill ranked {kv}")
+
+
+def test_prefill_many_sequences_in_index_order(pa):
+    # more than 64 sequences are taken in index order (one wave ranks up to 64)
+    n = 128
+    rng = np.random.default_rng(941)
+    lens = [int(x) for x in rng.integers(n, n + 90, size=66)]
+    case = small_case("bf16", n, 1, 1, lens, seed=941)
+    check(run(pa, case, "prefill"), run_oracle(case), "bf16", "prefill B=66")
+
+
 def test_prefill_workload_structure_in_fp32(pa):
     """Same shape in fp32 (1e-5 gate; the partition kernel): the first chunk, fully causal."""
     case = W.workload("prefill", kv_dtype="f32", q_dtype="f32")

@@ -18,11 +18,11 @@
 //    Chunked prefill uses 4 waves x 2 tiles (128 rows), draft trees 4 waves
 //    x 1 tile (64 rows, few registers per wave), both with two key groups
 //    (below): a row block's chain of pairs, which sets its workgroup's time,
-//    is cut in two;
-//  * the keys are walked in steps of two pages (32 tokens).  The workgroup
-//    copies each pair once into a ring of four LDS stages with direct
-//    global-to-LDS loads, three pairs ahead of the one being consumed, so no
-//    register holds data in flight.  Pages keep the pool's layouts: a wave's
+//    is cut in two.  Chunked-prefill row blocks are dispatched heaviest first;
+//  * the keys are walked in pairs of pages (32 tokens), one pair per key group
+//    and step.  The workgroup copies each pair once into a ring of four LDS
+//    stages with direct global-to-LDS loads, three steps ahead of the one
+//    being consumed, so no register holds data in flight.  Pages keep the pool's layouts: a wave's
 //    K operand is one contiguous KiB per LDS read.  E4M3 pages are converted
 //    to bf16 (exactly) as operands are read, their scales applied to the
 //    scores and probabilities.  bf16 V operands come straight from LDS with

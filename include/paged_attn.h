@@ -113,7 +113,10 @@ typedef struct pa_plan {
     int32_t row_tiles;        /* 16-row MFMA tiles per workgroup */
     int32_t row_chunks;       /* workgroups needed to cover the G * n rows */
     int32_t waves;            /* waves per workgroup */
-    int32_t grid;             /* workgroups of the partition kernel */
+    int32_t grid;             /* work items: workgroups of the partition kernel (and of the
+                                 LDS-staged kernel on draft trees); the chunked-prefill
+                                 kernel runs min(grid, CUs) workgroups that take them in
+                                 turn, heaviest first */
     int32_t reduce;           /* 1 if the split-K reduce kernel runs */
     int32_t kernel;           /* 0: partition kernel (+ reduce); 1: LDS-staged kernel for
                                  chunked prefill (128 rows of one sequence and kv head per

@@ -261,6 +261,11 @@ pa_status run(const pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
         sa.num_splits = pl.num_splits;
         sa.part_pages = pl.partition_pages;
         sa.scale_log2 = a.scale_log2;
+        const int64_t items = (int64_t)batch * d.num_kv_heads * sa.row_blocks * sa.num_splits;
+        if (items < 1 || items > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+        // chunked prefill: one workgroup per CU (its LDS ring fills the CU), each
+        // taking its share of the row blocks in turn; draft trees: one per item
+        sa.workgroups = staged_tree ? (int32_t)items : (int32_t)std::min<int64_t>(items, cu_count());
         if ((e = launch_staged(sa, d.kv_dtype == PA_FP8_E4M3, staged_tree, st, e0, e1)) != hipSuccess)
             return hip_fail(e, "staged kernel launch");
     } else {

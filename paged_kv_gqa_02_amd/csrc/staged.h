@@ -31,6 +31,8 @@ struct StagedArgs {
     int32_t num_splits;         // context partitions of the longest sequence
     int32_t part_pages;         // pages per partition
     float scale_log2;           // scale * log2(e)
+    int32_t workgroups;         // launched: one per work item (draft trees), or up to one
+                                // per CU taking the items in turn (chunked prefill)
 };
 
 // rows of one (sequence, kv head) per workgroup: chunked prefill, draft trees
@@ -40,7 +42,8 @@ constexpr int kStagedTreeRows = 64;
 // prefill (one partition per sequence), draft-tree partitions
 constexpr int kStagedMaxPages = 2048;
 constexpr int kStagedTreeMaxPages = 512;
-// Launches the kernel on `st`; grid = batch * hkv * row_blocks * num_splits.
+// Launches the kernel on `st` with a.workgroups workgroups over the
+// batch * hkv * row_blocks * num_splits work items (one each for draft trees).
 // ev_begin / ev_end (either may be null) take the kernel's start and end times.
 hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end);

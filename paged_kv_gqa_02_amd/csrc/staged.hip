@@ -215,7 +215,10 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
     __shared__ __attribute__((aligned(8))) int32_t ids[kIds];
     __shared__ float scales[FP8 ? 2 * kIds : 1];   // k then v, per page of the block
 
-    const int t = threadIdx.x;
+    // (the index builtins: this file is built without IEEE mode, and the
+    // device library's threadIdx / blockIdx helpers, built with it, would be
+    // called rather than inlined)
+    const int t = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = t & (kWave - 1);
     // (read through readfirstlane, so that the compiler knows them to be
     // wave-uniform and keeps what derives from them in scalar registers)
@@ -225,463 +228,501 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
-    int sp, b, kh, rb, seq_len;
-    {
-        sp = blockIdx.x % a.num_splits;
-        const int rest = blockIdx.x / a.num_splits;
-        if constexpr (TREE) {
-            // (sequence, kv head) pairs in blockIdx order, one row block each
-            const int bh_count = a.batch * a.hkv;
-            const int bh = rest % bh_count;
-            rb = a.row_blocks - 1 - rest / bh_count;
-            kh = bh % a.hkv;
-            b = bh / a.hkv;
-            seq_len = a.seq_lens[b];
-        } else {
-            // Causal row blocks differ in work: a block of a sequence with c
-            // earlier tokens walks c / 32 + (its index + 1) * (tokens per block) / 32
-            // pairs, and a workgroup's time follows its pair count.  blockIdx
-            // takes the slots (sequence rank, row block) heaviest first,
-            // sequences ranked by length (longest first), so that the
-            // dispatcher hands the lightest work to the CUs that finish first
-            // (one workgroup per CU).  The kv head is blockIdx's fastest
-            // index: the row blocks of one (sequence, kv head) share blockIdx
-            // mod Hkv, hence one XCD and its L2 when Hkv is a multiple of 8.
-            kh = rest % a.hkv;
-            const int q = rest / a.hkv;
-            const int rank = q / a.row_blocks;
-            rb = a.row_blocks - 1 - (q - rank * a.row_blocks);
-            if (a.batch <= kWave) {
-                // rank sequences by length in one wave: lane u holds length u
-                const int mine = lane < a.batch ? a.seq_lens[lane] : INT_MIN;
-                int r = 0;
-                for (int u = 0; u < a.batch; ++u) {
-                    const int lu = __builtin_amdgcn_readlane(mine, u);
-                    r += (lu > mine || (lu == mine && u < lane)) ? 1 : 0;
-                }
-                const uint64_t hit = __ballot(lane < a.batch && r == rank);
-                b = hit ? (int)__builtin_ctzll(hit) : rank;   // (ranks are a permutation)
-                seq_len = __builtin_amdgcn_readlane(mine, b);
-            } else {
-                b = rank;                          // many sequences: index order
+    // Work items are (row block, partition) units, taken in rounds of W =
+    // a.workgroups: in round r, workgroup w takes item r * W + w, or
+    // r * W + W - 1 - w in odd rounds, so that the items (heaviest first)
+    // pair up heavy with light on each workgroup.  Draft trees launch one
+    // workgroup per item; chunked prefill one per CU, which then runs its
+    // items back to back with no dispatch in between.
+    const int items = a.batch * a.hkv * a.row_blocks * a.num_splits;
+    // chunked prefill with up to 64 sequences: lane u holds the length of
+    // sequence u and its rank by length (longest first, ties by index)
+    int my_rank = 0;
+    int mine = INT_MIN;
+    if constexpr (!TREE) {
+        if (a.batch <= kWave) {
+            mine = lane < a.batch ? a.seq_lens[lane] : INT_MIN;
+            for (int u = 0; u < a.batch; ++u) {
+                const int lu = __builtin_amdgcn_readlane(mine, u);
+                my_rank += (lu > mine || (lu == mine && u < lane)) ? 1 : 0;
+            }
+        }
+    }
+    auto item = [&](const int x) {
+        int sp, b, kh, rb, seq_len;
+        {
+            sp = x % a.num_splits;
+            const int rest = x / a.num_splits;
+            if constexpr (TREE) {
+                // (sequence, kv head) pairs in blockIdx order, one row block each
+                const int bh_count = a.batch * a.hkv;
+                const int bh = rest % bh_count;
+                rb = a.row_blocks - 1 - rest / bh_count;
+                kh = bh % a.hkv;
+                b = bh / a.hkv;
                 seq_len = a.seq_lens[b];
+            } else {
+                // Causal row blocks differ in work: a block of a sequence with c
+                // earlier tokens walks c / 32 + (its index + 1) * (tokens per block) / 32
+                // pairs, and a workgroup's time follows its pair count.  blockIdx
+                // takes the slots (sequence rank, row block) heaviest first,
+                // sequences ranked by length (longest first), so that the
+                // dispatcher hands the lightest work to the CUs that finish first
+                // (one workgroup per CU).  The kv head is blockIdx's fastest
+                // index: the row blocks of one (sequence, kv head) share blockIdx
+                // mod Hkv, hence one XCD and its L2 when Hkv is a multiple of 8.
+                kh = rest % a.hkv;
+                const int q = rest / a.hkv;
+                const int rank = q / a.row_blocks;
+                rb = a.row_blocks - 1 - (q - rank * a.row_blocks);
+                if (a.batch <= kWave) {
+                    const uint64_t hit = __ballot(lane < a.batch && my_rank == rank);
+                    b = hit ? (int)__builtin_ctzll(hit) : rank;   // (ranks are a permutation)
+                    seq_len = __builtin_amdgcn_readlane(mine, b);
+                } else {
+                    b = rank;                          // many sequences: index order
+                    seq_len = a.seq_lens[b];
+                }
             }
+            sp = uni(sp);
+            b = uni(b);
+            kh = uni(kh);
+            rb = uni(rb);
         }
-        sp = uni(sp);
-        b = uni(b);
-        kh = uni(kh);
-        rb = uni(rb);
-    }
 
-    // Every load of the prologue is issued before the first one is waited for:
-    // this partition's block-table entries, the query rows and their tree masks
-    // (only the sequence length decides what is used of them).
-    const int pg0 = sp * a.part_pages;
-    const int part = min(a.part_pages, MAXP);     // a larger partition is cut short
-    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-    constexpr int kIdLoads = (kIds + kThreads - 1) / kThreads;
-    // (unconditional loads from clamped, in-bounds addresses: under a lane
-    // mask the compiler would wait for each load before issuing the next)
-    int idv[kIdLoads];
+        // Every load of the prologue is issued before the first one is waited for:
+        // this partition's block-table entries, the query rows and their tree masks
+        // (only the sequence length decides what is used of them).
+        const int pg0 = sp * a.part_pages;
+        const int part = min(a.part_pages, MAXP);     // a larger partition is cut short
+        const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+        // Page ids are fetched and staged by the loader threads: in chunked
+        // prefill the waves of key groups 1 .., which are idle while group 0
+        // writes the previous item's output and so fetch the next item's ids
+        // meanwhile; every thread otherwise.  (Unconditional loads from
+        // clamped, in-bounds addresses: under a lane mask the compiler would
+        // wait for each load before issuing the next.)
+        constexpr bool kGroupLoaders = KG > 1 && !TREE;
+        constexpr int kLoaders = kGroupLoaders ? (KG - 1) * WAVES * kWave : kThreads;
+        const int lt = kGroupLoaders ? t - WAVES * kWave : t;      // < 0: not a loader
+        constexpr int kIdLoads = (kIds + kLoaders - 1) / kLoaders;
+        int idv[kIdLoads];
+        if (lt >= 0) {
 #pragma unroll
-    for (int k = 0; k < kIdLoads; ++k)
-        idv[k] = bt_row[min(pg0 + min(t + k * kThreads, part), a.max_pages - 1)];
-    const int row0 = rb * kRows;
-    const int wrow0 = row0 + wave * kRowsPerWave;
-    // query rows of this wave (MFMA B-operand layout: lane holds row l16 of a tile)
-    bf16x8 qf[TILES][4];
-    int qi[TILES];
-    uint64_t tmask[TILES];
-#pragma unroll
-    for (int tt = 0; tt < TILES; ++tt) {
-        const int r = wrow0 + tt * 16 + l16;
-        const bool valid = r < a.rows;
-        const int i = valid ? r / a.group : 0;
-        const int h = kh * a.group + (valid ? r - i * a.group : 0);
-        const uint16_t* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
-            qf[tt][c] = __builtin_bit_cast(bf16x8, valid ? x : u32x4{0u, 0u, 0u, 0u});
+            for (int k = 0; k < kIdLoads; ++k)
+                idv[k] = bt_row[min(pg0 + min(lt + k * kLoaders, part), a.max_pages - 1)];
         }
-        qi[tt] = valid ? i : -1;
-        if constexpr (TREE) {
-            const uint64_t mk = a.tree_mask[(int64_t)b * a.n + i];
-            tmask[tt] = valid ? mk : ~uint64_t(0);
-        }
-    }
-
-    // lengths clamped to what the block table describes: arrays that break the
-    // contract give wrong numbers, never a stray access
-    // (the values below are wave-uniform; readfirstlane keeps them, and the
-    // loop control and page addresses derived from them, in scalar registers
-    // where a division or a loaded value would otherwise leave them in VGPRs)
-    const int L = uni(max(min(seq_len, a.max_pages * kPage), 1));
-    const int seq_pages = (L + kPage - 1) / kPage;
-    const int nsplit_b = uni(min((seq_pages + a.part_pages - 1) / a.part_pages, a.num_splits));
-    if (sp >= nsplit_b) return;                   // this sequence has fewer partitions
-    const int last_row = min(row0 + kRows, a.rows) - 1;
-    const int first_limit = L - a.n;              // row 0 sees tokens 0 .. L - n (causal)
-    // keys the block needs: up to the causal limit of its last row, or all (tree)
-    const int key_end = TREE ? L : uni(max(min(L, first_limit + last_row / a.group + 1), 1));
-    const int pg_end = uni(min(pg0 + part, (key_end + kPage - 1) / kPage));
-    const int npairs = uni(max(pg_end - pg0 + 1, 0) / 2);
-    const int last = uni(seq_pages - 1 - pg0);    // the sequence's last page, partition-relative
-    // the last pair of a partition with an odd page count reaches one page
-    // into the next partition: keys from here on are masked like dead ones
-    const int tok_end = min(L, kPage * pg_end);
-    int lim[TILES];
+        const int row0 = rb * kRows;
+        const int wrow0 = row0 + wave * kRowsPerWave;
+        // query rows of this wave (MFMA B-operand layout: lane holds row l16 of a tile)
+        bf16x8 qf[TILES][4];
+        int qi[TILES];
+        uint64_t tmask[TILES];
 #pragma unroll
-    for (int tt = 0; tt < TILES; ++tt)
-        lim[tt] = qi[tt] >= 0 ? first_limit + qi[tt] : L - 1;   // padding rows see every live key
-    // the pairs that need masks: those past the smallest causal limit among
-    // this wave's rows, or reaching the tree tokens
-    const int wave_lim = TREE ? first_limit - 1 : uni(first_limit + min(wrow0, a.rows - 1) / a.group);
-
-    // page ids (and E4M3 scales) of the partition, clamped to the pool
-#pragma unroll
-    for (int k = 0; k < kIdLoads; ++k) {
-        const int p = t + k * kThreads;
-        if (p < 2 * npairs) {
-            const int id = min(max(idv[k], 0), a.num_pages - 1);
-            ids[p] = id;
-            if constexpr (FP8) {
-                scales[p] = a.k_scale[(int64_t)id * a.hkv + kh];
-                scales[kIds + p] = a.v_scale[(int64_t)id * a.hkv + kh];
-            }
-        }
-    }
-    __syncthreads();
-
-    f32x4 acc[TILES][8];
-    f32x4 lsum[TILES];      // bf16 pools: row sums of the weights, from an all-ones MFMA
-    float m[TILES], l[TILES];
-#pragma unroll
-    for (int tt = 0; tt < TILES; ++tt) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) acc[tt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m[tt] = kNoMax;
-        l[tt] = 0.f;
-    }
-    // A operand of all ones (bf16 1.0 = 0x3F80): C[m][row] = sum over the 32
-    // tokens of the row's weights, exactly the bf16 values that enter PV
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
-                                                         0x3F803F80u});
-
-    // Scores of pair jp for every tile, raw: K operands of both pages from LDS,
-    // QK^T on the MFMAs.  The scale (and an E4M3 page's K scale) is folded into
-    // the exponent later: p = exp2(s * f - m) with f > 0, so max(s * f) = f * max(s).
-    auto scores = [&](const uint8_t* st, float (&sc)[TILES][8]) {
-        u32x4 kf[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int tt = 0; tt < TILES; ++tt) {
+            const int r = wrow0 + tt * 16 + l16;
+            const bool valid = r < a.rows;
+            const int i = valid ? r / a.group : 0;
+            const int h = kh * a.group + (valid ? r - i * a.group : 0);
+            const uint16_t* qrow = a.q + (((int64_t)b * a.n + i) * a.hq + h) * kHeadDim;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint8_t* kp = st + h * Ly::kPageBytes;
-                if constexpr (FP8)
-                    kf[h][c] = k_operand_fp8(kp, c, l16, g);
-                else
-                    kf[h][c] = *reinterpret_cast<const u32x4*>(kp + 1024 * c + 16 * lane);
+                const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+                qf[tt][c] = __builtin_bit_cast(bf16x8, valid ? x : u32x4{0u, 0u, 0u, 0u});
             }
-        // MFMA runs at raised wave priority, here and for PV: a wave about to
-        // issue MFMAs goes first, and the other waves of the SIMD fill its
-        // MFMA time with their softmax arithmetic (about 2 % on prefill)
-        __builtin_amdgcn_s_setprio(1);
+            qi[tt] = valid ? i : -1;
+            if constexpr (TREE) {
+                const uint64_t mk = a.tree_mask[(int64_t)b * a.n + i];
+                tmask[tt] = valid ? mk : ~uint64_t(0);
+            }
+        }
+
+        // lengths clamped to what the block table describes: arrays that break the
+        // contract give wrong numbers, never a stray access
+        // (the values below are wave-uniform; readfirstlane keeps them, and the
+        // loop control and page addresses derived from them, in scalar registers
+        // where a division or a loaded value would otherwise leave them in VGPRs)
+        const int L = uni(max(min(seq_len, a.max_pages * kPage), 1));
+        const int seq_pages = (L + kPage - 1) / kPage;
+        const int nsplit_b = uni(min((seq_pages + a.part_pages - 1) / a.part_pages, a.num_splits));
+        if (sp >= nsplit_b) return;                   // this sequence has fewer partitions
+        const int last_row = min(row0 + kRows, a.rows) - 1;
+        const int first_limit = L - a.n;              // row 0 sees tokens 0 .. L - n (causal)
+        // keys the block needs: up to the causal limit of its last row, or all (tree)
+        const int key_end = TREE ? L : uni(max(min(L, first_limit + last_row / a.group + 1), 1));
+        const int pg_end = uni(min(pg0 + part, (key_end + kPage - 1) / kPage));
+        const int npairs = uni(max(pg_end - pg0 + 1, 0) / 2);
+        const int last = uni(seq_pages - 1 - pg0);    // the sequence's last page, partition-relative
+        // the last pair of a partition with an odd page count reaches one page
+        // into the next partition: keys from here on are masked like dead ones
+        const int tok_end = min(L, kPage * pg_end);
+        int lim[TILES];
 #pragma unroll
         for (int tt = 0; tt < TILES; ++tt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[h][c]),
-                                                                 qf[tt][c], s4, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) sc[tt][4 * h + v] = s4[v];
-            }
-        __builtin_amdgcn_s_setprio(0);
-    };
+            lim[tt] = qi[tt] >= 0 ? first_limit + qi[tt] : L - 1;   // padding rows see every live key
+        // the pairs that need masks: those past the smallest causal limit among
+        // this wave's rows, or reaching the tree tokens
+        const int wave_lim = TREE ? first_limit - 1 : uni(first_limit + min(wrow0, a.rows - 1) / a.group);
 
-    // step j holds pairs KG j .. KG j + KG - 1, pair KG j + k in sub-stage k;
-    // key group k copies and computes pair KG j + k
-    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    const int nsteps = KG == 1 ? npairs : (npairs + KG - 1) / KG;
-    // prologue: steps 0 .. kStages - 2 in flight.  No step past the last is
-    // copied, so the loads outstanding after step j are those of the
-    // min(kStages - 2, nsteps - 1 - j) steps that follow it.
+        // page ids (and E4M3 scales) of the partition, clamped to the pool
 #pragma unroll
-    for (int j = 0; j < kStages - 1; ++j)
-        if (j < nsteps)
-            issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * j + kg, kh, wave, lane,
-                                         lds0 + j * kStep + kg * Ly::kStage);
-
-    for (int j = 0; j < nsteps; ++j) {
-        // this wave's part of step j has landed once at most the later steps'
-        // loads are outstanding; the barrier then covers every wave's part, and
-        // every wave is done with step j - 1, whose stage is refilled next
-        wait_steps<kStages - 2, Ly::kLoadsPerWave>(min(kStages - 2, nsteps - 1 - j));
-        __syncthreads();
-        if (j + kStages - 1 < nsteps)
-            issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * (j + kStages - 1) + kg, kh,
-                                         wave, lane, lds0 + ((j + kStages - 1) % kStages) * kStep +
-                                                         kg * Ly::kStage);
-
-        const int step_base = 16 * pg0 + 32 * KG * j;     // first token of the step
-        if (step_base + 32 * KG - 1 >= L) {
-            // the step holding the sequence end: V rows past it may hold NaN,
-            // which a zero weight would still carry through the MFMA, so they
-            // are zeroed in LDS (once per workgroup, on this step only)
-            constexpr int kRowBytes = kHeadDim * Ly::kElem;
-            constexpr int kChunks = 32 * kRowBytes / 16;   // 16-byte pieces of a pair's V rows
-            for (int e = t; e < KG * kChunks; e += kThreads) {
-                const int sub = KG == 1 ? 0 : e / kChunks;
-                const int ep = KG == 1 ? e : e % kChunks;
-                const int tok = ep / (kRowBytes / 16);
-                if (step_base + 32 * sub + tok >= L)
-                    *reinterpret_cast<u32x4*>(lds + (j % kStages) * kStep + sub * Ly::kStage +
-                                              (2 + tok / 16) * Ly::kPageBytes + (tok % 16) * kRowBytes +
-                                              16 * (ep % (kRowBytes / 16))) = u32x4{0u, 0u, 0u, 0u};
-            }
-            __syncthreads();
-        }
-        const int jp = KG * j + kg;               // this wave's pair
-        if constexpr (KG > 1)
-            if (jp >= npairs) continue;           // (a key group past the end idles)
-        uint8_t* st = lds + (j % kStages) * kStep + kg * Ly::kStage;
-        const int base = 16 * pg0 + 32 * jp;      // first token of the pair
-        const bool need_mask = base + 31 > wave_lim || base + 31 >= tok_end;
-        float sc[TILES][8];
-        scores(st, sc);
-        float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
-        if constexpr (FP8) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int pg = min(2 * jp + h, last);
-                ks[h] = scales[pg];
-                vs[h] = scales[kIds + pg];
-            }
-        }
-        // V operands over the 32 tokens: {page 0 rows 4g..4g+3, page 1 rows 4g..4g+3}
-        bf16x8 va[8];
-        {
-            i16x4 av[2][8];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint8_t* vp = st + (2 + h) * Ly::kPageBytes;
+        for (int k = 0; k < kIdLoads; ++k) {
+            const int p = lt + k * kLoaders;
+            if (lt >= 0 && p < 2 * npairs) {
+                const int id = min(max(idv[k], 0), a.num_pages - 1);
+                ids[p] = id;
                 if constexpr (FP8) {
-                    // a[db] = {V[4g + s][8 l16 + db], s = 0..3}: rows read, then permuted
-                    u32x4 vr[4];
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const u32x2 w = *reinterpret_cast<const u32x2*>(vp + (4 * g + s4) * kHeadDim + 8 * l16);
-                        vr[s4] = fp8x8_to_bf16x8(w[0], w[1]);
-                    }
-                    v_operands(av[h], vr);
-                } else {
-                    // a[db] = {V[4g + k][16 db + l16], k = 0..3} from one transposing
-                    // read: in each 16-lane group, lane j names 4 elements of row
-                    // 4g + j / 4 at dims 16 db + 4 (j % 4), and lane i receives the
-                    // i % 4-th element of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4
-                    const int row = 4 * g + (l16 >> 2);
-                    const uint8_t* rp = vp + 2 * kHeadDim * row + 8 * (l16 & 1);
-#pragma unroll
-                    for (int db = 0; db < 8; ++db) {
-                        const int chunk = 2 * db + ((l16 & 3) >> 1);
-                        av[h][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(rp + 16 * (chunk ^ vswz(row))));
-                    }
+                    scales[p] = a.k_scale[(int64_t)id * a.hkv + kh];
+                    scales[kIds + p] = a.v_scale[(int64_t)id * a.hkv + kh];
                 }
             }
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-                va[db] = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(av[0][db], av[1][db], 0, 1, 2, 3, 4, 5, 6, 7));
         }
-        float f[2];
+        __syncthreads();
+
+        f32x4 acc[TILES][8];
+        f32x4 lsum[TILES];      // bf16 pools: row sums of the weights, from an all-ones MFMA
+        float m[TILES], l[TILES];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) f[h] = FP8 ? a.scale_log2 * ks[h] : a.scale_log2;
-        if (need_mask) {
+        for (int tt = 0; tt < TILES; ++tt) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) acc[tt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m[tt] = kNoMax;
+            l[tt] = 0.f;
+        }
+        // A operand of all ones (bf16 1.0 = 0x3F80): C[m][row] = sum over the 32
+        // tokens of the row's weights, exactly the bf16 values that enter PV
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                             0x3F803F80u});
+
+        // Scores of pair jp for every tile, raw: K operands of both pages from LDS,
+        // QK^T on the MFMAs.  The scale (and an E4M3 page's K scale) is folded into
+        // the exponent later: p = exp2(s * f - m) with f > 0, so max(s * f) = f * max(s).
+        auto scores = [&](const uint8_t* st, float (&sc)[TILES][8]) {
+            u32x4 kf[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint8_t* kp = st + h * Ly::kPageBytes;
+                    if constexpr (FP8)
+                        kf[h][c] = k_operand_fp8(kp, c, l16, g);
+                    else
+                        kf[h][c] = *reinterpret_cast<const u32x4*>(kp + 1024 * c + 16 * lane);
+                }
+            // MFMA runs at raised wave priority, here and for PV: a wave about to
+            // issue MFMAs goes first, and the other waves of the SIMD fill its
+            // MFMA time with their softmax arithmetic (about 2 % on prefill)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tok = base + 16 * (e >> 2) + 4 * g + (e & 3);
-                    bool vis;
-                    if constexpr (TREE)
-                        vis = tok < first_limit ||
-                              ((tmask[tt] >> min(max(tok - first_limit, 0), 63)) & 1u);
-                    else
-                        vis = tok <= lim[tt];
-                    vis = vis && tok < tok_end;
-                    sc[tt][e] = vis ? sc[tt][e] : -INFINITY;
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[h][c]),
+                                                                     qf[tt][c], s4, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sc[tt][4 * h + v] = s4[v];
                 }
-        }
-        // Phase 2: row maxima, and one rescale branch for all tiles (a tile
-        // whose maximum did not move is multiplied by exp2(0) = 1, exactly)
-        float mx[TILES];
-        bool grow_any = false;
-#pragma unroll
-        for (int tt = 0; tt < TILES; ++tt) {
-            float x = -INFINITY;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float ph = fmaxf(fmaxf(sc[tt][4 * h], sc[tt][4 * h + 1]),
-                                       fmaxf(sc[tt][4 * h + 2], sc[tt][4 * h + 3]));
-                x = fmaxf(x, ph * f[h]);
-            }
-            mx[tt] = group_max(x);
-            grow_any |= mx[tt] > m[tt] + kRescaleSlack;
-        }
-        if (__any(grow_any)) {
-#pragma unroll
-            for (int tt = 0; tt < TILES; ++tt) {
-                const float mnew = mx[tt] > m[tt] + kRescaleSlack ? mx[tt] : m[tt];
-                const float alpha = fast_exp2(m[tt] - mnew);
-                m[tt] = mnew;
-                l[tt] *= alpha;
-                lsum[tt] *= alpha;
-#pragma unroll
-                for (int db = 0; db < 8; ++db) acc[tt][db] *= alpha;
-            }
-        }
-        // Phase 3, one basic block: weights and PV of every tile, so that one
-        // tile's exponentials can issue while the other's MFMAs run
-#pragma unroll
-        for (int tt = 0; tt < TILES; ++tt) {
-            float pw[8];
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = fast_exp2(__builtin_fmaf(sc[tt][e], f[e >> 2], -m[tt]));
-                pw[e] = FP8 ? p * vs[e >> 2] : p;
-                if constexpr (FP8) psum += p;
-            }
-            const bf16x8 pf = __builtin_bit_cast(
-                bf16x8, u32x4{bf16x2_bits(pw[0], pw[1]), bf16x2_bits(pw[2], pw[3]),
-                              bf16x2_bits(pw[4], pw[5]), bf16x2_bits(pw[6], pw[7])});
-            if constexpr (FP8)
-                l[tt] += psum;      // the V scale rides on the weights, not on their sum
-            else
-                lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[tt], 0, 0, 0);
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-                acc[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, acc[tt][db], 0, 0, 0);
             __builtin_amdgcn_s_setprio(0);
-        }
-    }
-    // no copy may still be writing this workgroup's LDS when it exits
-    wait_dma<0>();
-    if constexpr (KG > 1) {
-        // key groups 1 .. KG - 1 hand their (max, sum, accumulator) to group 0
-        // through the ring, one tile at a time, value x of a lane at
-        // xs[x * kLanes + lane id] (consecutive lanes, consecutive words);
-        // group 0 merges them with weights 2^(m_k - max) and writes the result
-        constexpr int kLanes = (KG - 1) * WAVES * kWave;
-        constexpr int kVals = 34;                  // acc (32), m, l of one tile
-        float* xs = reinterpret_cast<float*>(lds);
-        static_assert(kLanes * kVals * 4 <= kStages * kStep, "merge fits the ring");
-        __syncthreads();                           // every wave is done with the ring
+        };
+
+        // step j holds pairs KG j .. KG j + KG - 1, pair KG j + k in sub-stage k;
+        // key group k copies and computes pair KG j + k
+        const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+        const int nsteps = KG == 1 ? npairs : (npairs + KG - 1) / KG;
+        // prologue: steps 0 .. kStages - 2 in flight.  No step past the last is
+        // copied, so the loads outstanding after step j are those of the
+        // min(kStages - 2, nsteps - 1 - j) steps that follow it.
 #pragma unroll
-        for (int tt = 0; tt < TILES; ++tt) {
-            if (kg > 0) {
-                float* my = xs + ((kg - 1) * WAVES + wave) * kWave + lane;
+        for (int j = 0; j < kStages - 1; ++j)
+            if (j < nsteps)
+                issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * j + kg, kh, wave, lane,
+                                             lds0 + j * kStep + kg * Ly::kStage);
+
+        for (int j = 0; j < nsteps; ++j) {
+            // this wave's part of step j has landed once at most the later steps'
+            // loads are outstanding; the barrier then covers every wave's part, and
+            // every wave is done with step j - 1, whose stage is refilled next
+            wait_steps<kStages - 2, Ly::kLoadsPerWave>(min(kStages - 2, nsteps - 1 - j));
+            __syncthreads();
+            if (j + kStages - 1 < nsteps)
+                issue_pair<FP8, WAVES, TREE>(a, ids, npairs, last, KG * (j + kStages - 1) + kg, kh,
+                                             wave, lane, lds0 + ((j + kStages - 1) % kStages) * kStep +
+                                                             kg * Ly::kStage);
+
+            const int step_base = 16 * pg0 + 32 * KG * j;     // first token of the step
+            if (step_base + 32 * KG - 1 >= L) {
+                // the step holding the sequence end: V rows past it may hold NaN,
+                // which a zero weight would still carry through the MFMA, so they
+                // are zeroed in LDS (once per workgroup, on this step only)
+                constexpr int kRowBytes = kHeadDim * Ly::kElem;
+                constexpr int kChunks = 32 * kRowBytes / 16;   // 16-byte pieces of a pair's V rows
+                for (int e = t; e < KG * kChunks; e += kThreads) {
+                    const int sub = KG == 1 ? 0 : e / kChunks;
+                    const int ep = KG == 1 ? e : e % kChunks;
+                    const int tok = ep / (kRowBytes / 16);
+                    if (step_base + 32 * sub + tok >= L)
+                        *reinterpret_cast<u32x4*>(lds + (j % kStages) * kStep + sub * Ly::kStage +
+                                                  (2 + tok / 16) * Ly::kPageBytes + (tok % 16) * kRowBytes +
+                                                  16 * (ep % (kRowBytes / 16))) = u32x4{0u, 0u, 0u, 0u};
+                }
+                __syncthreads();
+            }
+            const int jp = KG * j + kg;               // this wave's pair
+            if constexpr (KG > 1)
+                if (jp >= npairs) continue;           // (a key group past the end idles)
+            uint8_t* st = lds + (j % kStages) * kStep + kg * Ly::kStage;
+            const int base = 16 * pg0 + 32 * jp;      // first token of the pair
+            const bool need_mask = base + 31 > wave_lim || base + 31 >= tok_end;
+            float sc[TILES][8];
+            scores(st, sc);
+            float ks[2] = {1.f, 1.f}, vs[2] = {1.f, 1.f};
+            if constexpr (FP8) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int pg = min(2 * jp + h, last);
+                    ks[h] = scales[pg];
+                    vs[h] = scales[kIds + pg];
+                }
+            }
+            // V operands over the 32 tokens: {page 0 rows 4g..4g+3, page 1 rows 4g..4g+3}
+            bf16x8 va[8];
+            {
+                i16x4 av[2][8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint8_t* vp = st + (2 + h) * Ly::kPageBytes;
+                    if constexpr (FP8) {
+                        // a[db] = {V[4g + s][8 l16 + db], s = 0..3}: rows read, then permuted
+                        u32x4 vr[4];
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            const u32x2 w = *reinterpret_cast<const u32x2*>(vp + (4 * g + s4) * kHeadDim + 8 * l16);
+                            vr[s4] = fp8x8_to_bf16x8(w[0], w[1]);
+                        }
+                        v_operands(av[h], vr);
+                    } else {
+                        // a[db] = {V[4g + k][16 db + l16], k = 0..3} from one transposing
+                        // read: in each 16-lane group, lane j names 4 elements of row
+                        // 4g + j / 4 at dims 16 db + 4 (j % 4), and lane i receives the
+                        // i % 4-th element of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4
+                        const int row = 4 * g + (l16 >> 2);
+                        const uint8_t* rp = vp + 2 * kHeadDim * row + 8 * (l16 & 1);
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) {
+                            const int chunk = 2 * db + ((l16 & 3) >> 1);
+                            av[h][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) i16x4*)(rp + 16 * (chunk ^ vswz(row))));
+                        }
+                    }
+                }
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) my[(4 * db + v) * kLanes] = acc[tt][db][v];
-                my[32 * kLanes] = m[tt];
-                my[33 * kLanes] = FP8 ? l[tt] : lsum[tt][0];
+                    va[db] = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(av[0][db], av[1][db], 0, 1, 2, 3, 4, 5, 6, 7));
             }
-            __syncthreads();
-            if (kg == 0) {
-                float mm = m[tt];
+            float f[2];
 #pragma unroll
-                for (int k = 1; k < KG; ++k)
-                    mm = fmaxf(mm, xs[32 * kLanes + ((k - 1) * WAVES + wave) * kWave + lane]);
-                const float s0 = fast_exp2(m[tt] - mm);
-                float lt = (FP8 ? l[tt] : lsum[tt][0]) * s0;
+            for (int h = 0; h < 2; ++h) f[h] = FP8 ? a.scale_log2 * ks[h] : a.scale_log2;
+            if (need_mask) {
 #pragma unroll
-                for (int db = 0; db < 8; ++db) acc[tt][db] *= s0;
+                for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
-                for (int k = 1; k < KG; ++k) {
-                    const float* o = xs + ((k - 1) * WAVES + wave) * kWave + lane;
-                    const float sk = fast_exp2(o[32 * kLanes] - mm);
-                    lt += o[33 * kLanes] * sk;
+                    for (int e = 0; e < 8; ++e) {
+                        const int tok = base + 16 * (e >> 2) + 4 * g + (e & 3);
+                        bool vis;
+                        if constexpr (TREE)
+                            vis = tok < first_limit ||
+                                  ((tmask[tt] >> min(max(tok - first_limit, 0), 63)) & 1u);
+                        else
+                            vis = tok <= lim[tt];
+                        vis = vis && tok < tok_end;
+                        sc[tt][e] = vis ? sc[tt][e] : -INFINITY;
+                    }
+            }
+            // Phase 2: row maxima, and one rescale branch for all tiles (a tile
+            // whose maximum did not move is multiplied by exp2(0) = 1, exactly)
+            float mx[TILES];
+            bool grow_any = false;
 #pragma unroll
-                    for (int db = 0; db < 8; ++db)
+            for (int tt = 0; tt < TILES; ++tt) {
+                float x = -INFINITY;
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[tt][db][v] += o[(4 * db + v) * kLanes] * sk;
+                for (int h = 0; h < 2; ++h) {
+                    const float ph = fmaxf(fmaxf(sc[tt][4 * h], sc[tt][4 * h + 1]),
+                                           fmaxf(sc[tt][4 * h + 2], sc[tt][4 * h + 3]));
+                    x = fmaxf(x, ph * f[h]);
                 }
-                m[tt] = mm;
+                mx[tt] = group_max(x);
+                grow_any |= mx[tt] > m[tt] + kRescaleSlack;
+            }
+            if (__any(grow_any)) {
+#pragma unroll
+                for (int tt = 0; tt < TILES; ++tt) {
+                    const float mnew = mx[tt] > m[tt] + kRescaleSlack ? mx[tt] : m[tt];
+                    const float alpha = fast_exp2(m[tt] - mnew);
+                    m[tt] = mnew;
+                    l[tt] *= alpha;
+                    lsum[tt] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) acc[tt][db] *= alpha;
+                }
+            }
+            // Phase 3, one basic block: weights and PV of every tile, so that one
+            // tile's exponentials can issue while the other's MFMAs run
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+                float pw[8];
+                float psum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = fast_exp2(__builtin_fmaf(sc[tt][e], f[e >> 2], -m[tt]));
+                    pw[e] = FP8 ? p * vs[e >> 2] : p;
+                    if constexpr (FP8) psum += p;
+                }
+                const bf16x8 pf = __builtin_bit_cast(
+                    bf16x8, u32x4{bf16x2_bits(pw[0], pw[1]), bf16x2_bits(pw[2], pw[3]),
+                                  bf16x2_bits(pw[4], pw[5]), bf16x2_bits(pw[6], pw[7])});
                 if constexpr (FP8)
-                    l[tt] = lt;
+                    l[tt] += psum;      // the V scale rides on the weights, not on their sum
                 else
-                    lsum[tt][0] = lt;
+                    lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[tt], 0, 0, 0);
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    acc[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf, acc[tt][db], 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
             }
-            if (tt + 1 < TILES) __syncthreads();   // group 0 is done reading the slots
         }
-        if (kg > 0) return;
-    }
-
-    // epilogue: lane holds O[row l16][32 g + 8 v + db] (E4M3 pools) or
-    // O[row l16][16 db + 4 g + v] (bf16 pools) of each tile; the final output
-    // when the sequence has one partition, else this partition's partial
-    const bool single = nsplit_b == 1;
+        // no copy may still be writing this workgroup's LDS when it exits
+        wait_dma<0>();
+        if constexpr (KG > 1) {
+            // key groups 1 .. KG - 1 hand their (max, sum, accumulator) to group 0
+            // through the ring, one tile at a time, value x of a lane at
+            // xs[x * kLanes + lane id] (consecutive lanes, consecutive words);
+            // group 0 merges them with weights 2^(m_k - max) and writes the result
+            constexpr int kLanes = (KG - 1) * WAVES * kWave;
+            constexpr int kVals = 34;                  // acc (32), m, l of one tile
+            float* xs = reinterpret_cast<float*>(lds);
+            static_assert(kLanes * kVals * 4 <= kStages * kStep, "merge fits the ring");
+            __syncthreads();                           // every wave is done with the ring
 #pragma unroll
-    for (int tt = 0; tt < TILES; ++tt) {
-        const int r = wrow0 + tt * 16 + l16;
-        const float lt = FP8 ? group_sum(l[tt]) : lsum[tt][0];
-        if (r < a.rows) {
-            const int i = r / a.group;
-            const int h = kh * a.group + (r - i * a.group);
-            const int64_t orow = ((int64_t)b * a.n + i) * a.hq + h;
-            if (single) {
-                const float inv = 1.0f / lt;
-                uint16_t* o = a.out + orow * kHeadDim;
-                if constexpr (FP8) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        uint32_t w[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            w[e] = bf16x2_bits(acc[tt][2 * e][v] * inv, acc[tt][2 * e + 1][v] * inv);
-                        *reinterpret_cast<u32x4*>(o + 32 * g + 8 * v) = u32x4{w[0], w[1], w[2], w[3]};
-                    }
-                } else {
-#pragma unroll
-                    for (int db = 0; db < 8; ++db) {
-                        const f32x4 x = acc[tt][db] * inv;
-                        *reinterpret_cast<u32x2*>(o + 16 * db + 4 * g) =
-                            u32x2{bf16x2_bits(x[0], x[1]), bf16x2_bits(x[2], x[3])};
-                    }
-                }
-            } else {
-                const int64_t pidx = orow * a.num_splits + sp;
-                float* pa = a.part_acc + pidx * kHeadDim;
-                if constexpr (FP8) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        f32x4 lo, hi;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            lo[e] = acc[tt][e][v];
-                            hi[e] = acc[tt][4 + e][v];
-                        }
-                        *reinterpret_cast<f32x4*>(pa + 32 * g + 8 * v) = lo;
-                        *reinterpret_cast<f32x4*>(pa + 32 * g + 8 * v + 4) = hi;
-                    }
-                } else {
+            for (int tt = 0; tt < TILES; ++tt) {
+                if (kg > 0) {
+                    float* my = xs + ((kg - 1) * WAVES + wave) * kWave + lane;
 #pragma unroll
                     for (int db = 0; db < 8; ++db)
-                        *reinterpret_cast<f32x4*>(pa + 16 * db + 4 * g) = acc[tt][db];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) my[(4 * db + v) * kLanes] = acc[tt][db][v];
+                    my[32 * kLanes] = m[tt];
+                    my[33 * kLanes] = FP8 ? l[tt] : lsum[tt][0];
                 }
-                if (g == 0) {
-                    a.part_ml[pidx * 2] = m[tt];
-                    a.part_ml[pidx * 2 + 1] = lt;
+                __syncthreads();
+                if (kg == 0) {
+                    float mm = m[tt];
+#pragma unroll
+                    for (int k = 1; k < KG; ++k)
+                        mm = fmaxf(mm, xs[32 * kLanes + ((k - 1) * WAVES + wave) * kWave + lane]);
+                    const float s0 = fast_exp2(m[tt] - mm);
+                    float lt = (FP8 ? l[tt] : lsum[tt][0]) * s0;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) acc[tt][db] *= s0;
+#pragma unroll
+                    for (int k = 1; k < KG; ++k) {
+                        const float* o = xs + ((k - 1) * WAVES + wave) * kWave + lane;
+                        const float sk = fast_exp2(o[32 * kLanes] - mm);
+                        lt += o[33 * kLanes] * sk;
+#pragma unroll
+                        for (int db = 0; db < 8; ++db)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) acc[tt][db][v] += o[(4 * db + v) * kLanes] * sk;
+                    }
+                    m[tt] = mm;
+                    if constexpr (FP8)
+                        l[tt] = lt;
+                    else
+                        lsum[tt][0] = lt;
+                }
+                if (tt + 1 < TILES) __syncthreads();   // group 0 is done reading the slots
+            }
+        }
+
+        // epilogue: lane holds O[row l16][32 g + 8 v + db] (E4M3 pools) or
+        // O[row l16][16 db + 4 g + v] (bf16 pools) of each tile; the final output
+        // when the sequence has one partition, else this partition's partial
+        const bool single = nsplit_b == 1;
+        if (kg == 0) {    // (the other key groups handed their states to group 0)
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+                const int r = wrow0 + tt * 16 + l16;
+                const float lt = FP8 ? group_sum(l[tt]) : lsum[tt][0];
+                if (r < a.rows) {
+                    const int i = r / a.group;
+                    const int h = kh * a.group + (r - i * a.group);
+                    const int64_t orow = ((int64_t)b * a.n + i) * a.hq + h;
+                    if (single) {
+                        const float inv = 1.0f / lt;
+                        uint16_t* o = a.out + orow * kHeadDim;
+                        if constexpr (FP8) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                uint32_t w[4];
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    w[e] = bf16x2_bits(acc[tt][2 * e][v] * inv, acc[tt][2 * e + 1][v] * inv);
+                                *reinterpret_cast<u32x4*>(o + 32 * g + 8 * v) = u32x4{w[0], w[1], w[2], w[3]};
+                            }
+                        } else {
+#pragma unroll
+                            for (int db = 0; db < 8; ++db) {
+                                const f32x4 x = acc[tt][db] * inv;
+                                *reinterpret_cast<u32x2*>(o + 16 * db + 4 * g) =
+                                    u32x2{bf16x2_bits(x[0], x[1]), bf16x2_bits(x[2], x[3])};
+                            }
+                        }
+                    } else {
+                        const int64_t pidx = orow * a.num_splits + sp;
+                        float* pa = a.part_acc + pidx * kHeadDim;
+                        if constexpr (FP8) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                f32x4 lo, hi;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    lo[e] = acc[tt][e][v];
+                                    hi[e] = acc[tt][4 + e][v];
+                                }
+                                *reinterpret_cast<f32x4*>(pa + 32 * g + 8 * v) = lo;
+                                *reinterpret_cast<f32x4*>(pa + 32 * g + 8 * v + 4) = hi;
+                            }
+                        } else {
+#pragma unroll
+                            for (int db = 0; db < 8; ++db)
+                                *reinterpret_cast<f32x4*>(pa + 16 * db + 4 * g) = acc[tt][db];
+                        }
+                        if (g == 0) {
+                            a.part_ml[pidx * 2] = m[tt];
+                            a.part_ml[pidx * 2 + 1] = lt;
+                        }
+                    }
                 }
             }
+        }
+        // (one key group: no merge barrier separates this item's last reads of
+        // the page ids from the next item's writes)
+        if constexpr (KG == 1) __syncthreads();
+    };
+    if constexpr (TREE) {
+        item((int)__builtin_amdgcn_workgroup_id_x());
+    } else {
+        const int wgs = a.workgroups;
+        const int w = (int)__builtin_amdgcn_workgroup_id_x();
+        for (int x0 = 0; x0 < items; x0 += wgs) {
+            const int x = x0 + (((x0 / wgs) & 1) ? wgs - 1 - w : w);
+            if (x < items) item(x);
         }
     }
 }
@@ -703,7 +744,7 @@ hipError_t launch(const StagedArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0,
 hipError_t launch_staged(const StagedArgs& a, bool fp8, bool tree, hipStream_t st,
                          hipEvent_t e0, hipEvent_t e1)
 {
-    const dim3 grid((unsigned)((int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits));
+    const dim3 grid((unsigned)a.workgroups);
     if (tree)
         return fp8 ? launch<true, 4, 1, true, kRing, kStagedTreeMaxPages, kTreeKeyGroups>(a, grid, st,
                                                                                         e0, e1)

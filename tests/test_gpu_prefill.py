@@ -85,6 +85,16 @@ def test_prefill_many_sequences_in_index_order(pa):
     check(run(pa, case, "prefill"), run_oracle(case), "bf16", "prefill B=66")
 
 
+def test_prefill_items_in_several_rounds(pa):
+    # 40 sequences x 8 kv heads x 2 row blocks = 640 items over one workgroup
+    # per CU: a forward round, a reversed round and a partial third one
+    n = 128
+    rng = np.random.default_rng(942)
+    lens = [int(x) for x in rng.integers(n, n + 64, size=40)]
+    case = small_case("bf16", n, 16, 8, lens, seed=942)
+    check(run(pa, case, "prefill"), run_oracle(case), "bf16", "prefill 640 items")
+
+
 def test_prefill_workload_structure_in_fp32(pa):
     """Same shape in fp32 (1e-5 gate; the partition kernel): the first chunk, fully causal."""
     case = W.workload("prefill", kv_dtype="f32", q_dtype="f32")

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
             sp = x % a.num_splits;
             const int rest = x / a.num_splits;
             if constexpr (TREE) {
-                // (sequence, kv head) pairs in blockIdx order, one row block each
+                // (sequence, kv head) pairs in item order, one row block each
                 const int bh_count = a.batch * a.hkv;
                 const int bh = rest % bh_count;
                 rb = a.row_blocks - 1 - rest / bh_count;
@@ -264,13 +264,12 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
             } else {
                 // Causal row blocks differ in work: a block of a sequence with c
                 // earlier tokens walks c / 32 + (its index + 1) * (tokens per block) / 32
-                // pairs, and a workgroup's time follows its pair count.  blockIdx
-                // takes the slots (sequence rank, row block) heaviest first,
-                // sequences ranked by length (longest first), so that the
-                // dispatcher hands the lightest work to the CUs that finish first
-                // (one workgroup per CU).  The kv head is blockIdx's fastest
-                // index: the row blocks of one (sequence, kv head) share blockIdx
-                // mod Hkv, hence one XCD and its L2 when Hkv is a multiple of 8.
+                // pairs, and an item's time follows its pair count.  Items take
+                // the slots (sequence rank, row block) heaviest first, sequences
+                // ranked by length (longest first).  The kv head is the items'
+                // fastest index: the row blocks of one (sequence, kv head) share
+                // item mod Hkv, hence (rounds being multiples of 8 workgroups
+                // wide) one XCD and its L2 when Hkv is a multiple of 8.
                 kh = rest % a.hkv;
                 const int q = rest / a.hkv;
                 const int rank = q / a.row_blocks;
@@ -597,7 +596,7 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
                 __builtin_amdgcn_s_setprio(0);
             }
         }
-        // no copy may still be writing this workgroup's LDS when it exits
+        // no copy may still be writing this item's ring when it is reused
         wait_dma<0>();
         if constexpr (KG > 1) {
             // key groups 1 .. KG - 1 hand their (max, sum, accumulator) to group 0

@@ -268,8 +268,9 @@ __global__ __launch_bounds__(WAVES * KG * kWave, 2) void paged_attn_staged(Stage
                 // the slots (sequence rank, row block) heaviest first, sequences
                 // ranked by length (longest first).  The kv head is the items'
                 // fastest index: the row blocks of one (sequence, kv head) share
-                // item mod Hkv, hence (rounds being multiples of 8 workgroups
-                // wide) one XCD and its L2 when Hkv is a multiple of 8.
+                // item mod Hkv, so with workgroups placed round-robin on the 8
+                // XCDs (and a multiple of 8 of them) they run on two XCDs at most,
+                // one per round direction, whose L2s serve their re-reads.
                 kh = rest % a.hkv;
                 const int q = rest / a.hkv;
                 const int rank = q / a.row_blocks;

@@ -99,20 +99,31 @@ def attention_flops(case):
     return 4 * case.head_dim * case.num_q_heads * int(keys)
 
 
+def code_digest(path):
+    """sha256 of a C / HIP source with its comments and whitespace removed: it
+    changes when the code does, not when a comment does."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    # string and character literals are kept; comments are dropped
+    token = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    code = token.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()
+
+
 def measured_traffic(key):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter runs (profiles/traffic.json), if they were taken on the kernel
-    source as it is now (else None)."""
-    import hashlib
+    code as it is now (else None)."""
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         rec = json.load(open(os.path.join(root, "profiles", "traffic.json"))).get(key)
         if not rec:
             return None
-        digest = hashlib.sha256(open(os.path.join(root, rec["source"]), "rb").read()).hexdigest()
+        digest = code_digest(os.path.join(root, rec["source"]))
     except (OSError, ValueError, KeyError):
         return None
-    if rec.get("source_sha256") != digest:
+    if rec.get("code_sha256") != digest:
         return None
     return int(round(rec["traffic_bytes"]))
 

@@ -150,11 +150,38 @@ def cpu_baseline(case, reps):
             times.append(time.perf_counter() - t0)
             log(f"cpu baseline rep {r}: {times[-1]:.2f} s")
     t = float(np.median(times))
-    return {"value": case.algorithmic_bytes() / t / 1e9, "unit": "GB/s", "cores": cores,
+    used = min(cores, case.batch)             # one sequence per thread
+    # the same oracle on one thread, over the first sequences that fit a few seconds
+    t1 = time.perf_counter()
+    one(0)
+    t1 = time.perf_counter() - t1
+    k = int(max(1, min(case.batch, 4.0 / max(t1, 1e-6))))
+    if k > 1:
+        t1 = time.perf_counter()
+        for b in range(k):
+            one(b)
+        t1 = time.perf_counter() - t1
+    log(f"cpu baseline, one thread: {k} sequences in {t1:.2f} s")
+    return {"value": case.algorithmic_bytes() / t / 1e9, "unit": "GB/s", "cores": used,
             "kind": "oracle",
             "sample": f"whole batch ({case.batch} sequences, every head and row) x {reps} reps, "
                       f"median {t:.3f} s, float64 C oracle, one sequence per thread",
-            "tokens_per_s": case.batch * case.q_per_seq / t}
+            "tokens_per_s": case.batch * case.q_per_seq / t,
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": case.algorithmic_bytes(seqs=range(k)) / t1 / 1e9,
+                              "unit": "GB/s", "cores": 1,
+                              "sample": f"sequences 0..{k - 1} of {case.batch}, once, {t1:.2f} s"}}
+
+
+def cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def append_bytes(case, n_new, src_dtype, seq_lens=None):

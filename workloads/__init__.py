@@ -246,23 +246,27 @@ class Case:
     def max_pages(self) -> int:
         return int(self.block_table.shape[1])
 
-    def kv_bytes(self) -> int:
-        """Bytes of K and V for every token of every sequence (+ fp8 scales)."""
+    def kv_bytes(self, seqs=None) -> int:
+        """Bytes of K and V for every token of every sequence (or of the
+        sequences `seqs`), + fp8 scales."""
+        lens = self.seq_lens if seqs is None else self.seq_lens[list(seqs)]
         esz = {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
-        toks = int(self.seq_lens.astype(np.int64).sum())
+        toks = int(lens.astype(np.int64).sum())
         b = 2 * toks * self.num_kv_heads * self.head_dim * esz
         if self.kv_dtype == "fp8":
-            pages = sum(pages_for(x) for x in self.seq_lens)
+            pages = sum(pages_for(x) for x in lens)
             b += 2 * pages * self.num_kv_heads * 4
         return b
 
-    def q_bytes(self) -> int:
+    def q_bytes(self, seqs=None) -> int:
         esz = {"f32": 4, "bf16": 2}[self.q_dtype]
-        return self.batch * self.q_per_seq * self.num_q_heads * self.head_dim * esz
+        nseq = self.batch if seqs is None else len(list(seqs))
+        return nseq * self.q_per_seq * self.num_q_heads * self.head_dim * esz
 
-    def algorithmic_bytes(self) -> int:
-        """KV (+ scales) read once per (sequence, kv head), Q read once, O written once."""
-        return self.kv_bytes() + 2 * self.q_bytes()
+    def algorithmic_bytes(self, seqs=None) -> int:
+        """KV (+ scales) read once per (sequence, kv head), Q read once, O written
+        once: for the whole batch, or for the sequences `seqs`."""
+        return self.kv_bytes(seqs) + 2 * self.q_bytes(seqs)
 
 
 def _valid_slots(block_table, seq_lens, num_pages):

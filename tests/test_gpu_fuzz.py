@@ -18,7 +18,7 @@ from test_gpu_parity import check, run_gpu, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
-NUM_CASES = 40
+NUM_CASES = 100
 
 
 @pytest.fixture(scope="module")

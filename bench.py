@@ -397,7 +397,7 @@ def measure_copy_gbs(torch, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+        print("bench.py: this benchmark runs on one GPU only (there is no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch

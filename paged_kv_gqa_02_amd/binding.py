@@ -148,11 +148,12 @@ def _stream(stream) -> ctypes.c_void_p:
 class Pool:
     """Handle of a page pool; keeps the pool tensors alive while it lives."""
 
-    def __init__(self, handle, tensors, num_pages, num_kv_heads):
+    def __init__(self, handle, tensors, num_pages, num_kv_heads, kv_dtype):
         self.handle = handle
         self._tensors = tensors
         self.num_pages = num_pages
         self.num_kv_heads = num_kv_heads
+        self.kv_dtype = kv_dtype
 
     def close(self):
         if self.handle:
@@ -183,6 +184,10 @@ def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_sca
     float32, bfloat16 or fp8 bytes)."""
     if v.dim() != 4 or k.dtype != v.dtype or k.numel() != v.numel() or k.shape[:2] != v.shape[:2]:
         raise ValueError("v must be [num_pages][Hkv][16][128] and k the same elements, chunked")
+    if _kv_code(k) == PA_FP8_E4M3:
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if sc is None or sc.dtype != torch.float32 or sc.numel() != v.shape[0] * v.shape[1]:
+                raise ValueError(f"{name} must be float32 with num_pages * Hkv entries")
     desc = pa_pool_desc(num_pages=v.shape[0], page_size=v.shape[2], num_kv_heads=v.shape[1],
                         head_dim=v.shape[3], kv_dtype=_kv_code(k), k=_dptr(k), v=_dptr(v),
                         k_scale=_dptr(k_scale), v_scale=_dptr(v_scale),
@@ -191,7 +196,7 @@ def paged_attn_create_pool(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_sca
     h = ctypes.c_void_p()
     _check(_lib.paged_attn_create_pool(ctypes.byref(desc), ctypes.byref(h)),
            "paged_attn_create_pool")
-    return Pool(h, (k, v, k_scale, v_scale), v.shape[0], v.shape[1])
+    return Pool(h, (k, v, k_scale, v_scale), v.shape[0], v.shape[1], _kv_code(k))
 
 
 def paged_attn_destroy_pool(pool: Pool):
@@ -224,14 +229,25 @@ def workspace_for(pool: Pool, q: torch.Tensor, max_seq_len: int) -> Optional[tor
     return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
-def _shapes(q, block_table, seq_lens):
-    if q.dim() != 4:
-        raise ValueError("q must be [batch][q_per_seq][Hq][128]")
-    batch = q.shape[0]
+HEAD_DIM = 128
+
+
+def _tables(batch, block_table, seq_lens):
     if block_table.dim() != 2 or block_table.shape[0] != batch or block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32 [batch][max_pages]")
     if seq_lens.shape != (batch,) or seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32 [batch]")
+
+
+def _shapes(pool, q, block_table, seq_lens):
+    """Checks what the library reads through raw pointers and cannot check itself:
+    the tensors' extents (head dim, query heads) and the table dtypes."""
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM:
+        raise ValueError("q must be [batch][q_per_seq][Hq][128]")
+    if q.shape[2] % pool.num_kv_heads != 0:
+        raise ValueError("the query heads must be a multiple of the pool's KV heads")
+    batch = q.shape[0]
+    _tables(batch, block_table, seq_lens)
     return batch
 
 
@@ -242,7 +258,7 @@ def paged_attn_verify(pool: Pool, q: torch.Tensor, out: torch.Tensor, block_tabl
                       ) -> torch.Tensor:
     """q, out: [batch][q_per_seq][Hq][128]; returns out.  With events (HipEvent)
     or a tree mask this goes through paged_attn_verify_timed."""
-    batch = _shapes(q, block_table, seq_lens)
+    batch = _shapes(pool, q, block_table, seq_lens)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
     if tree_mask is not None and (tree_mask.shape != (batch, q.shape[1])
@@ -270,7 +286,7 @@ def paged_attn_verify_tree(pool: Pool, q: torch.Tensor, out: torch.Tensor,
                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Draft-tree verification; tree_mask: [batch][q_per_seq] uint64 ancestor masks
     (a torch.int64 / torch.uint64 device tensor holding the bit patterns)."""
-    batch = _shapes(q, block_table, seq_lens)
+    batch = _shapes(pool, q, block_table, seq_lens)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
     if tree_mask.shape != (batch, q.shape[1]) or tree_mask.element_size() != 8:
@@ -300,7 +316,7 @@ def paged_attn_decode(pool: Pool, q: torch.Tensor, out: torch.Tensor, block_tabl
     o4 = out if out.dim() == 4 else out.unsqueeze(1)
     if q4.shape[1] != 1:
         raise ValueError("decode takes one query row per sequence")
-    batch = _shapes(q4, block_table, seq_lens)
+    batch = _shapes(pool, q4, block_table, seq_lens)
     if o4.shape != q4.shape or o4.dtype != q4.dtype:
         raise ValueError("out must match q in shape and dtype")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -316,11 +332,11 @@ def paged_attn_append_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor,
                          block_table: torch.Tensor, seq_lens: torch.Tensor, stream=None):
     """Write the n_new newest tokens ([batch][n_new][Hkv][128], float32 or bfloat16)
     of every sequence into the pool (fp8 pools: quantize-on-write)."""
-    if k_new.shape != v_new.shape or k_new.dim() != 4 or k_new.dtype != v_new.dtype:
-        raise ValueError("k_new and v_new must both be [batch][n_new][Hkv][128]")
+    if (k_new.shape != v_new.shape or k_new.dim() != 4 or k_new.dtype != v_new.dtype
+            or k_new.shape[2] != pool.num_kv_heads or k_new.shape[3] != HEAD_DIM):
+        raise ValueError("k_new and v_new must both be [batch][n_new][Hkv][128], Hkv the pool's")
     batch, n_new = k_new.shape[0], k_new.shape[1]
-    if block_table.dim() != 2 or block_table.shape[0] != batch or seq_lens.shape != (batch,):
-        raise ValueError("block_table / seq_lens must have one row per sequence")
+    _tables(batch, block_table, seq_lens)
     _check(_lib.paged_attn_append_kv(pool.handle, _dptr(k_new), _dptr(v_new), _q_code(k_new),
                                      _dptr(block_table), block_table.shape[1], _dptr(seq_lens),
                                      batch, n_new, _stream(stream)),
@@ -364,6 +380,10 @@ def paged_attn_rejection_sample(p: torch.Tensor, q: Optional[torch.Tensor],
         tokens = torch.empty((batch, k1), dtype=torch.int32, device=p.device)
     if num_accepted is None:
         num_accepted = torch.empty((batch,), dtype=torch.int32, device=p.device)
+    if tokens.shape != (batch, k1) or tokens.dtype != torch.int32:
+        raise ValueError("tokens must be int32 [batch][K+1]")
+    if num_accepted.shape != (batch,) or num_accepted.dtype != torch.int32:
+        raise ValueError("num_accepted must be int32 [batch]")
     ws_bytes = paged_attn_rejection_sample_workspace_bytes(batch, vocab)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=p.device)

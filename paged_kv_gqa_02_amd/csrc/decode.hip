@@ -352,6 +352,7 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
     // (unconditional loads from clamped, in-bounds addresses: a lane-masked
     // load would make the compiler wait for it on the spot)
+    // (the first round of this wave's page ids: see the pipeline below)
     const int raw_id = bt_row[min(pg0 + wave + lane * W, min(pg0 + a.part_pages, a.max_pages) - 1)];
     QFrag<KV> qf[NT];
     int qi[NT];
@@ -408,9 +409,12 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
         l[nt] = 0.f;
     }
 
-    // this wave's pages: pg0 + wave + j * W, j < nj (nj <= 64 by construction)
+    // this wave's pages: pg0 + wave + j * W, j < nj.  A lane holds one page id,
+    // so the wave takes its ids in rounds of 64 pages; the next round's ids are
+    // requested when a round starts.  Automatic plans keep nj <= 64 (one round)
+    // up to 64 * W * kMaxSplits pages per sequence.
     const int nj = (pg1 - pg0 - wave + W - 1) / W;
-    const int my_id = (lane < nj) ? min(max(raw_id, 0), a.num_pages - 1) : 0;
+    const int id_last = min(pg0 + a.part_pages, a.max_pages) - 1;
 
     auto consume = [&](Page<KV>& pg, int j) {
         const int base = (pg0 + wave + j * W) * kPage;
@@ -461,24 +465,29 @@ __global__ __launch_bounds__(W * kWave, (min_waves_per_simd<KV, NT, PF>())) void
     };
 
     // Software pipeline: page j + PF - 1 is requested before page j is used.
-    // Loads are unconditional (indices past the last page repeat the last
+    // Loads are unconditional (indices past the round's last page repeat that
     // page) so that the wait before each use covers only that page's loads.
-    if (nj > 0) {
-        auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(my_id, min(j, nj - 1)); };
+    int ids = raw_id;                               // round 0: requested with the length
+    for (int r0 = 0; r0 < nj; r0 += kWave) {
+        const int nr = min(nj - r0, kWave);
+        const int my_id = (lane < nr) ? min(max(ids, 0), a.num_pages - 1) : 0;
+        if (r0 + kWave < nj)
+            ids = bt_row[min(pg0 + wave + (r0 + kWave + lane) * W, id_last)];
+        auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(my_id, min(j, nr - 1)); };
         Page<KV> buf[PF];
 #pragma unroll
         for (int st = 0; st < PF - 1; ++st) load_page(buf[st], a, phys_of(st), kh, l16, g);
         int j0 = 0;
-        for (; j0 + PF <= nj; j0 += PF) {
+        for (; j0 + PF <= nr; j0 += PF) {
 #pragma unroll
             for (int st = 0; st < PF; ++st) {
                 load_page(buf[(st + PF - 1) % PF], a, phys_of(j0 + st + PF - 1), kh, l16, g);
-                consume(buf[st], j0 + st);
+                consume(buf[st], r0 + j0 + st);
             }
         }
 #pragma unroll
         for (int st = 0; st < PF - 1; ++st)
-            if (j0 + st < nj) consume(buf[st], j0 + st);
+            if (j0 + st < nr) consume(buf[st], r0 + j0 + st);
     }
 
     // ---- merge the waves of this workgroup (fixed order) ----

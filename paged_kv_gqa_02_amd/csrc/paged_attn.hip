@@ -120,6 +120,7 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
     const int64_t row_chunks = (rows + 16 * nt - 1) / (16 * nt);
     const int max_pages = (max_len + kPage - 1) / kPage;
     const int64_t units = (int64_t)batch * d.num_kv_heads * row_chunks;
+    const int waves = d.waves > 0 ? d.waves : kDefaultWaves;
     int part;
     if (d.partition_pages > 0) {
         part = std::min(d.partition_pages, max_pages);
@@ -128,13 +129,16 @@ pa_status make_plan(const pa_pool* pool, int32_t batch, int32_t n, int32_t hq, i
         // whose workgroups already fill the register file (MI355X sweep)
         const int64_t target = (nt == 1 ? 2LL : 1LL) * cu_count();
         int64_t ns = (target + units - 1) / units;
-        const int64_t ns_cap =
-            std::max<int64_t>(1, max_pages / (2 * (d.waves > 0 ? d.waves : kDefaultWaves)));
+        const int64_t ns_cap = std::max<int64_t>(1, max_pages / (2 * waves));
         ns = std::max<int64_t>(1, std::min(ns, ns_cap));
         part = (int)((max_pages + ns - 1) / ns);
+        // a wave takes its page ids 64 at a time: keep automatic partitions to
+        // one round per wave while the split count allows
+        part = std::min(part, 64 * waves);
     }
-    const int waves = d.waves > 0 ? d.waves : kDefaultWaves;
-    part = std::min(part, 64 * waves);         // each wave holds at most 64 page ids
+    // at most kMaxSplits partitions: longer sequences (more than 64 * W *
+    // kMaxSplits pages) and partitions the pool asks for give a wave more than
+    // 64 pages, which the partition kernel takes in several rounds of ids
     part = std::max(part, (max_pages + kMaxSplits - 1) / kMaxSplits);
     const int64_t ns = (max_pages + part - 1) / part;
     const int64_t grid = units * ns;

@@ -229,3 +229,28 @@ def test_workspace_covers_tree_calls_when_prefill_plan_is_reported():
     assert ws.value >= need.value > 0
     LIB.paged_attn_destroy_pool(h)
     LIB.paged_attn_destroy_pool(h2)
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("max_len", [262160, 524304, 1 << 20])
+def test_long_context_plans_take_page_id_rounds(waves, max_len):
+    """Past 64 * W * 64 pages the automatic plan stays at 64 partitions, so a
+    wave walks more than 64 pages and the partition kernel takes its page ids in
+    rounds of 64 (checked against the oracle on the GPU at 270,000 tokens)."""
+    st, h = _create(num_pages=1 << 16, waves=waves)
+    assert st == 0
+    pl = _plan(h, 1, 1, 32, max_len)
+    pages = (max_len + 15) // 16
+    assert pl.num_splits == 64 and pl.num_splits * pl.partition_pages >= pages
+    assert pl.kernel == 0 and pl.waves == waves
+    assert pl.partition_pages > 64 * waves or pages <= 64 * 64 * waves
+    LIB.paged_attn_destroy_pool(h)
+
+
+def test_pool_partition_request_is_kept():
+    """A partition length the pool asks for is used as given, also above 64
+    pages per wave (the kernel then takes its page ids in rounds)."""
+    st, h = _create(num_pages=8192, partition_pages=1000)
+    pl = _plan(h, 2, 1, 32, 16 * 4001)
+    assert pl.partition_pages == 1000 and pl.num_splits == 5
+    LIB.paged_attn_destroy_pool(h)

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle_parallel import oracle_all
 from workloads.device import to_device, to_numpy_f64
 from test_gpu_parity import MAX_ABS, check, run_oracle, say, small_case
 
@@ -96,17 +97,21 @@ def test_prefill_items_in_several_rounds(pa):
 
 
 def test_prefill_workload_structure_in_fp32(pa):
-    """Same shape in fp32 (1e-5 gate; the partition kernel): the first chunk, fully causal."""
+    """Same shape in fp32 (1e-5 gate; the partition kernel), every sequence: the
+    chunks after 1536, 1024 and 512 earlier tokens and the first chunk."""
     case = W.workload("prefill", kv_dtype="f32", q_dtype="f32")
     gpu = run(pa, case, "partition")
-    check(gpu[3:4], run_oracle(case, seqs=[3]), "f32", "prefill fp32 seq 3")
+    check(gpu, oracle_all(case), "f32", "prefill fp32, all 4 chunks")
 
 
 @pytest.mark.parametrize("kernel", ["prefill", "partition"])
 def test_prefill_workload_native(pa, kernel):
     case = W.workload("prefill")
     gpu = run(pa, case, kernel)
-    check(gpu[3:4], run_oracle(case, seqs=[3]), "bf16", f"prefill bf16 seq 3 {kernel}")
+    ref = oracle_all(case)
+    for b in range(case.batch):
+        ctx = int(case.seq_lens[b]) - case.q_per_seq
+        check(gpu[b:b + 1], ref[b:b + 1], "bf16", f"prefill bf16 seq {b} ({ctx} earlier) {kernel}")
 
 
 def test_prefill_kernels_agree_at_the_workload(pa):

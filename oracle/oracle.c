@@ -387,20 +387,113 @@ int oracle_append_kv(void* k_pool, void* v_pool, int kv_dtype, float* k_scale, f
     return ORACLE_OK;
 }
 
-/* inverse-CDF draw from non-negative weights w[0..V): the smallest j whose
- * running (left-to-right, binary64) sum exceeds u * total; -1 if total is 0 */
-static int32_t draw(const double* w, int V, float u)
+/* ---- exact integers for the draw --------------------------------------
+ * Every float32 is an integer multiple of 2^-149, below 2^128.  A weight,
+ * a running sum of up to 2^20 weights, and the products compared below all
+ * fit in 16 little-endian 32-bit limbs (512 bits). */
+#define BIG_LIMBS 16
+typedef struct { uint32_t d[BIG_LIMBS]; } big;
+
+static void big_zero(big* a) { memset(a, 0, sizeof *a); }
+
+static int big_is_zero(const big* a)
 {
-    double total = 0.0;
-    for (int j = 0; j < V; ++j) total += w[j];
-    if (!(total > 0.0)) return -1;
-    const double target = (double)u * total;
-    double run = 0.0;
-    for (int j = 0; j < V; ++j) {
-        run += w[j];
-        if (run > target) return j;
+    for (int i = 0; i < BIG_LIMBS; ++i)
+        if (a->d[i]) return 0;
+    return 1;
+}
+
+/* a = |x| / 2^-149 (x finite); the bits of x give it exactly: significand
+ * (with the hidden bit for normal numbers) times 2^(exponent field - 1) */
+static void big_from_f32(big* a, float x)
+{
+    uint32_t bits;
+    memcpy(&bits, &x, sizeof bits);
+    const uint32_t e = (bits >> 23) & 0xffu;
+    const uint64_t m = (bits & 0x7fffffu) | (e ? 0x800000u : 0u);
+    const uint32_t s = e ? e - 1 : 0;
+    big_zero(a);
+    const uint64_t shifted = m << (s % 32);          /* at most 55 bits */
+    a->d[s / 32] = (uint32_t)shifted;
+    if (s / 32 + 1 < BIG_LIMBS) a->d[s / 32 + 1] = (uint32_t)(shifted >> 32);
+}
+
+static int big_cmp(const big* a, const big* b)
+{
+    for (int i = BIG_LIMBS - 1; i >= 0; --i)
+        if (a->d[i] != b->d[i]) return a->d[i] > b->d[i] ? 1 : -1;
+    return 0;
+}
+
+static void big_add(big* a, const big* b)           /* a += b */
+{
+    uint64_t carry = 0;
+    for (int i = 0; i < BIG_LIMBS; ++i) {
+        const uint64_t t = (uint64_t)a->d[i] + b->d[i] + carry;
+        a->d[i] = (uint32_t)t;
+        carry = t >> 32;
     }
-    return -1;   /* unreachable: run ends at total > target */
+}
+
+static void big_sub(big* a, const big* b)           /* a -= b, for a >= b */
+{
+    int64_t borrow = 0;
+    for (int i = 0; i < BIG_LIMBS; ++i) {
+        int64_t t = (int64_t)a->d[i] - b->d[i] - borrow;
+        borrow = t < 0;
+        a->d[i] = (uint32_t)(t + (borrow ? ((int64_t)1 << 32) : 0));
+    }
+}
+
+static void big_shl(big* out, const big* a, int s)  /* out = a * 2^s */
+{
+    big r;
+    big_zero(&r);
+    for (int i = BIG_LIMBS - 1; i >= 0; --i) {
+        const int j = i - s / 32;
+        if (j < 0) continue;
+        uint64_t v = (uint64_t)a->d[j] << (s % 32);
+        if (s % 32 && j > 0) v |= (uint64_t)a->d[j - 1] >> (32 - s % 32);
+        r.d[i] = (uint32_t)v;
+    }
+    *out = r;
+}
+
+static void big_mul_small(big* out, const big* a, uint32_t m)   /* out = a * m */
+{
+    uint64_t carry = 0;
+    for (int i = 0; i < BIG_LIMBS; ++i) {
+        const uint64_t t = (uint64_t)a->d[i] * m + carry;
+        out->d[i] = (uint32_t)t;
+        carry = t >> 32;
+    }
+}
+
+/* Inverse-CDF draw from the non-negative weights w[0..V): the smallest j with
+ * w_0 + ... + w_j > u * (w_0 + ... + w_{V-1}), decided exactly.  With u = U *
+ * 2^-149 (U an integer, from u's bits), the test is
+ * (w_0 + ... + w_j) * 2^149 > U * total, in integers.  -1 if the total is 0. */
+static int32_t draw(const big* w, int V, float u)
+{
+    big total, rhs, run, lhs;
+    big_zero(&total);
+    for (int j = 0; j < V; ++j) big_add(&total, &w[j]);
+    if (big_is_zero(&total)) return -1;
+    /* rhs = U * total: u's significand times total, shifted by u's exponent
+     * (U < 2^149 because 0 <= u < 1) */
+    uint32_t ubits;
+    memcpy(&ubits, &u, sizeof ubits);
+    const uint32_t e = (ubits >> 23) & 0xffu;
+    const uint32_t m = (ubits & 0x7fffffu) | (e ? 0x800000u : 0u);
+    big_mul_small(&rhs, &total, m);
+    big_shl(&rhs, &rhs, e ? (int)e - 1 : 0);
+    big_zero(&run);
+    for (int j = 0; j < V; ++j) {
+        big_add(&run, &w[j]);
+        big_shl(&lhs, &run, 149);
+        if (big_cmp(&lhs, &rhs) > 0) return j;
+    }
+    return -1;   /* unreachable: run ends at total and total * 2^149 > U * total */
 }
 
 int oracle_rejection_sample(const float* p, const float* q, const int32_t* draft,
@@ -410,7 +503,11 @@ int oracle_rejection_sample(const float* p, const float* q, const int32_t* draft
     if (batch < 0 || K < 0 || V < 1) return ORACLE_BAD_ARG;
     for (size_t i = 0; i < (size_t)batch * K; ++i)
         if (draft[i] < 0 || draft[i] >= V) return ORACLE_BAD_ARG;
-    double* w = (double*)malloc(sizeof(double) * (size_t)V);
+    for (size_t i = 0; i < (size_t)batch * (K + 1) * V; ++i)
+        if (!(p[i] >= 0.0f) || isinf(p[i])) return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < (size_t)batch * K * V; ++i)
+        if (!(q[i] >= 0.0f) || isinf(q[i])) return ORACLE_BAD_ARG;
+    big* w = (big*)malloc(sizeof(big) * (size_t)V);
     if (!w) return ORACLE_NO_MEMORY;
     for (int b = 0; b < batch; ++b) {
         const float* pb = p + (size_t)b * (K + 1) * V;
@@ -431,17 +528,20 @@ int oracle_rejection_sample(const float* p, const float* q, const int32_t* draft
         int32_t tok;
         if (r < K) {
             const float* qr = qb + (size_t)r * V;
-            for (int j = 0; j < V; ++j) {
-                const double d = (double)pr[j] - (double)qr[j];
-                w[j] = d > 0.0 ? d : 0.0;
+            for (int j = 0; j < V; ++j) {      /* w = max(0, p - q), exactly */
+                big qj;
+                big_from_f32(&w[j], pr[j]);
+                big_from_f32(&qj, qr[j]);
+                if (big_cmp(&w[j], &qj) > 0) big_sub(&w[j], &qj);
+                else big_zero(&w[j]);
             }
             tok = draw(w, V, u_sample[b]);
             if (tok < 0) {                      /* no residual mass: p itself */
-                for (int j = 0; j < V; ++j) w[j] = pr[j];
+                for (int j = 0; j < V; ++j) big_from_f32(&w[j], pr[j]);
                 tok = draw(w, V, u_sample[b]);
             }
         } else {
-            for (int j = 0; j < V; ++j) w[j] = pr[j];
+            for (int j = 0; j < V; ++j) big_from_f32(&w[j], pr[j]);
             tok = draw(w, V, u_sample[b]);
         }
         out[r] = tok;

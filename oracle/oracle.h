@@ -166,13 +166,16 @@ int oracle_append_kv(void* k_pool, void* v_pool, int kv_dtype, float* k_scale, f
  *       if it sums to 0, w = p[b][r]),
  *   w = p[b][K]                     when all K drafts are accepted (the bonus),
  * by inverse CDF: the smallest j with w_0 + ... + w_j > u_sample[b] * sum(w),
- * every sum taken left to right in binary64.  A row with no mass gives -1.
+ * decided exactly: every float32 is an integer multiple of 2^-149, so the
+ * weights, their sums and u * sum(w) are compared as integers (multi-limb,
+ * no rounding).  A row with no mass gives -1.
  * Sources: "Latency and cost in production" §10.6.2 (accept if p >= q, else
  * with probability p/q; on rejection sample from norm(max(0, p - q)); bonus
  * token when every draft passes) and "Speculative decoding principles"
  * (7.2.1), acceptance rule (a uniform u is drawn and the draft passes iff
  * u < p/q) and residual distribution.
- * Returns ORACLE_BAD_ARG for K < 0, V < 1 or a draft token outside [0, V).
+ * Returns ORACLE_BAD_ARG for K < 0, V < 1, a draft token outside [0, V), or
+ * an entry of p or q that is negative, infinite or NaN.
  */
 int oracle_rejection_sample(const float* p, const float* q, const int32_t* draft,
                             const float* u_accept, const float* u_sample,

@@ -237,3 +237,154 @@ def test_rejects_out_of_range_drafts():
     with pytest.raises(ValueError):
         oracle.rejection_sample(p, p[:, :1], np.array([[3]], np.int32),
                                 np.array([[0.5]], np.float32), np.array([0.5], np.float32))
+
+
+# ----------------------------------------------------------------------------
+# the draw is exact: pinned against rational arithmetic (Python's fractions)
+# ----------------------------------------------------------------------------
+def fraction_reference(p, q, draft, u_accept, u_sample):
+    """The acceptance step written out over exact rationals: the draft tests
+    u * q(x) < p(x), then the first j whose running sum of the weights exceeds
+    u * (their total), with p, q and u taken at their exact float32 values."""
+    B, k1, V = p.shape
+    K = k1 - 1
+    tokens = np.full((B, k1), -1, dtype=np.int64)
+    acc = np.zeros(B, dtype=np.int64)
+
+    def inverse_cdf(w, u):
+        total = sum(w, Fraction(0))
+        if total == 0:
+            return -1
+        target = Fraction(float(u)) * total
+        run = Fraction(0)
+        for j, wj in enumerate(w):
+            run += wj
+            if run > target:
+                return j
+        raise AssertionError("running sum never passed the target")
+
+    for b in range(B):
+        r = 0
+        while r < K:
+            x = int(draft[b, r])
+            if not Fraction(float(u_accept[b, r])) * Fraction(float(q[b, r, x])) < \
+                    Fraction(float(p[b, r, x])):
+                break
+            tokens[b, r] = x
+            r += 1
+        acc[b] = r
+        prow = [Fraction(float(v)) for v in p[b, r]]
+        if r < K:
+            qrow = [Fraction(float(v)) for v in q[b, r]]
+            tok = inverse_cdf([max(Fraction(0), a - c) for a, c in zip(prow, qrow)], u_sample[b])
+            if tok < 0:
+                tok = inverse_cdf(prow, u_sample[b])
+        else:
+            tok = inverse_cdf(prow, u_sample[b])
+        tokens[b, r] = tok
+    return tokens, acc
+
+
+def wide_range_rows(rng, shape):
+    """float32 values spread over the whole non-negative range below 2^22:
+    subnormals, tiny normals, ordinary probabilities and large values, zeros."""
+    mant = rng.integers(1 << 23, 1 << 24, size=shape).astype(np.float64)
+    expo = rng.choice([-170, -149, -140, -126, -100, -60, -30, -20, -10, -3, 0, 8],
+                      size=shape) + rng.integers(-3, 4, size=shape)
+    vals = np.ldexp(mant, expo - 23).astype(np.float32)
+    vals[rng.random(shape) < 0.2] = 0.0
+    return vals
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23, 24])
+def test_draw_equals_rational_reference(seed):
+    rng = np.random.default_rng(seed)
+    B, K, V = 200, 3, 24
+    p = wide_range_rows(rng, (B, K + 1, V))
+    q = wide_range_rows(rng, (B, K, V))
+    draft = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    # some drafts pass for sure (q = 0 at the draft) and some rows have an empty residual
+    q[:B // 4, :, :] = np.where(np.arange(V)[None, None, :] == draft[:B // 4, :, None], 0.0,
+                                q[:B // 4])
+    q[B // 4:B // 4 + 10, 0] = p[B // 4:B // 4 + 10, 0]
+    p[B // 4 + 10:B // 4 + 15] = 0.0                         # no mass at all: -1
+    ua = rng.random((B, K), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    us[:20] = np.float32(0.0)
+    us[20:40] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    tokens, acc = oracle.rejection_sample(p, q, draft, ua, us)
+    want_t, want_a = fraction_reference(p, q, draft, ua, us)
+    assert (acc == want_a).all()
+    assert (tokens == want_t).all()
+
+
+def test_ties_at_running_sum_boundaries():
+    """u * total equal to a running sum: that entry is not drawn (the sum must
+    exceed the target), the next positive one is."""
+    p = np.array([[[0.25, 0.0, 0.25, 0.5]]], np.float32)
+    none = np.zeros((1, 0, 4), np.float32)
+    for u, want in ((0.0, 0), (0.25, 2), (0.5, 3), (0.75, 3)):
+        tokens, _ = oracle.rejection_sample(p, none, np.zeros((1, 0), np.int32),
+                                            np.zeros((1, 0), np.float32), np.array([u], np.float32))
+        assert tokens[0, 0] == want, (u, tokens)
+
+
+def test_draw_keeps_weights_that_binary64_sums_lose():
+    """Weights 1/2, 2^-80, 1/2 with u = 1/2: the target is 1/2 + 2^-81, which the
+    first running sum (1/2) does not exceed and the second (1/2 + 2^-80) does.
+    Summed in binary64, 1/2 + 2^-80 rounds to 1/2 and the third token comes out."""
+    p = np.array([[[0.5, 2.0 ** -80, 0.5]]], np.float32)
+    none = np.zeros((1, 0, 3), np.float32)
+    tokens, _ = oracle.rejection_sample(p, none, np.zeros((1, 0), np.int32),
+                                        np.zeros((1, 0), np.float32), np.array([0.5], np.float32))
+    assert tokens[0, 0] == 1
+    cdf = np.cumsum(p[0, 0].astype(np.float64))
+    assert np.searchsorted(cdf, 0.5 * cdf[-1], side="right") == 2     # what binary64 gives
+
+
+def test_residual_is_exact_below_binary64_resolution():
+    """p - q formed exactly: p = 1 + 2^-23 and q = 2^-140 at token 0, p = 2^-130 at
+    token 1 (q = 0).  With u = 2^-1 the target is far inside token 0; with u the
+    largest float32 below 1 it still is (token 0's share is 1 - 2^-130ish)."""
+    p = np.array([[[np.float32(1 + 2.0 ** -23), np.float32(2.0 ** -130)], [1.0, 0.0]]], np.float32)
+    q = np.array([[[np.float32(2.0 ** -140), 0.0]]], np.float32)
+    draft = np.array([[0]], np.int32)
+    top = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    for u in (np.float32(0.5), top):
+        tokens, acc = oracle.rejection_sample(p, q, draft, np.array([[top]], np.float32),
+                                              np.array([u], np.float32))
+        want_t, want_a = fraction_reference(p, q, draft, np.array([[top]], np.float32),
+                                            np.array([u], np.float32))
+        assert acc[0] == want_a[0] and tokens[0, 0] == want_t[0, 0]
+
+
+def test_rejects_negative_or_nonfinite_probabilities():
+    p = np.full((1, 2, 3), 1 / 3, np.float32)
+    for bad in (-0.1, np.inf, np.nan):
+        pb = p.copy()
+        pb[0, 1, 2] = bad
+        with pytest.raises(ValueError):
+            oracle.rejection_sample(pb, p[:, :1], np.array([[0]], np.int32),
+                                    np.array([[0.5]], np.float32), np.array([0.5], np.float32))
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_targets_inside_weights_binary64_cannot_hold(seed):
+    """Rows 1/2, t_1, ..., t_n, 1/2 with tiny t_i (2^-90 .. 2^-60) and u = 1/2: the
+    target 1/2 + (t_1 + ... + t_n) / 2 falls among the tiny tokens, where the
+    rational reference and the oracle agree; binary64 running sums never leave 1/2
+    there and would give the last token."""
+    rng = np.random.default_rng(seed)
+    B, n = 64, 30
+    V = n + 2
+    p = np.zeros((B, 1, V), np.float32)
+    p[:, 0, 0] = p[:, 0, -1] = 0.5
+    mant = rng.integers(1 << 23, 1 << 24, size=(B, n)).astype(np.float64)
+    p[:, 0, 1:-1] = np.ldexp(mant, rng.integers(-90, -60, size=(B, n)) - 23).astype(np.float32)
+    none = np.zeros((B, 0, V), np.float32)
+    us = np.full(B, 0.5, np.float32)
+    tokens, _ = oracle.rejection_sample(p, none, np.zeros((B, 0), np.int32),
+                                        np.zeros((B, 0), np.float32), us)
+    want, _ = fraction_reference(p, none, np.zeros((B, 0), np.int32), np.zeros((B, 0)), us)
+    assert (tokens == want).all()
+    assert ((tokens[:, 0] >= 1) & (tokens[:, 0] <= n)).all()

@@ -205,6 +205,22 @@ pa_status paged_attn_verify_timed(const pa_pool* pool, const void* q, pa_dtype q
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   void* ev_begin, void* ev_end);
 
+/* paged_attn_verify for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument.  Split-K partials go to a static device
+ * array of the library, 16 MiB per GPU, held until the process ends; a shape
+ * whose partials need more (paged_attn_workspace_bytes) returns
+ * PA_ERR_WORKSPACE before anything runs.  The call allocates nothing; the
+ * first call on a device looks up the array's address there.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from several threads) race and give wrong results.  Otherwise
+ * as paged_attn_verify (causal mask; q_per_seq = 1 is a decode). */
+pa_status paged_attn_verify_noalloc(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                                    void* out, const int32_t* block_table,
+                                    int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                    int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                    int32_t num_q_heads, float scale, void* stream);
+
 /* KV append (quantize-on-write), the step before attention in a decode or
  * verify pass: writes the n_new newest tokens of each sequence (positions
  * L - n_new .. L - 1, L = seq_lens[b], which counts them) into the pool, in its

@@ -74,6 +74,8 @@ def _load():
                                    ctypes.c_float, vp, sz, vp]),
         "paged_attn_verify_timed": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32,
                                          i32, ctypes.c_float, vp, vp, sz, vp, vp, vp]),
+        "paged_attn_verify_noalloc": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32,
+                                           i32, ctypes.c_float, vp]),
         "paged_attn_verify_tree": (st, [vp, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32,
                                         i32, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_append_kv": (st, [vp, vp, vp, ctypes.c_int, vp, i32, vp, i32, i32, vp]),
@@ -277,6 +279,22 @@ def paged_attn_verify(pool: Pool, q: torch.Tensor, out: torch.Tensor, block_tabl
         _check(_lib.paged_attn_verify_timed(*head, _dptr(tree_mask), _dptr(workspace), ws_bytes,
                                             _stream(stream), hb, he),
                "paged_attn_verify_timed")
+    return out
+
+
+def paged_attn_verify_noalloc(pool: Pool, q: torch.Tensor, out: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor,
+                              max_seq_len: int, scale: float, stream=None) -> torch.Tensor:
+    """paged_attn_verify with the library's static split-K scratch (no workspace,
+    nothing allocated); calls that overlap on one GPU race.  Returns out."""
+    batch = _shapes(pool, q, block_table, seq_lens)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    _check(_lib.paged_attn_verify_noalloc(pool.handle, _dptr(q), _q_code(q), _dptr(out),
+                                          _dptr(block_table), block_table.shape[1],
+                                          _dptr(seq_lens), int(max_seq_len), batch, q.shape[1],
+                                          q.shape[2], float(scale), _stream(stream)),
+           "paged_attn_verify_noalloc")
     return out
 
 

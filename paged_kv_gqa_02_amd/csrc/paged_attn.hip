@@ -415,6 +415,62 @@ PA_API pa_status paged_attn_verify_tree(const pa_pool* pool, const void* q, pa_d
                nullptr, nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// paged_attn_verify_noalloc: the split-K partials in a static device array
+// ---------------------------------------------------------------------------
+// One copy per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+pa_status scratch_address(void** out)
+{
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+PA_API pa_status paged_attn_verify_noalloc(const pa_pool* pool, const void* q, pa_dtype q_dtype,
+                                           void* out, const int32_t* block_table,
+                                           int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                           int32_t max_seq_len, int32_t batch, int32_t q_per_seq,
+                                           int32_t num_q_heads, float scale, void* stream)
+{
+    // the partials the call's plan needs must fit the array; this is decided
+    // on the host before any HIP call
+    size_t need = 0;
+    pa_status st = paged_attn_workspace_bytes(pool, batch, q_per_seq, num_q_heads, max_seq_len,
+                                              &need);
+    if (st != PA_OK) return st;
+    if (need > kScratchBytes)
+        return fail(PA_ERR_WORKSPACE,
+                    "split-K partials exceed the 16 MiB static scratch; call paged_attn_verify "
+                    "with a workspace");
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws)) != PA_OK) return st;
+    return run(pool, q, q_dtype, out, block_table, max_pages_per_seq, seq_lens, max_seq_len, batch,
+               q_per_seq, num_q_heads, scale, nullptr, ws, need > 0 ? kScratchBytes : 0, stream,
+               nullptr, nullptr);
+}
+
 PA_API pa_status paged_attn_append_kv(const pa_pool* pool, const void* k_new, const void* v_new,
                                       pa_dtype src_dtype, const int32_t* block_table,
                                       int32_t max_pages_per_seq, const int32_t* seq_lens,

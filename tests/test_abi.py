@@ -254,3 +254,17 @@ def test_pool_partition_request_is_kept():
     pl = _plan(h, 2, 1, 32, 16 * 4001)
     assert pl.partition_pages == 1000 and pl.num_splits == 5
     LIB.paged_attn_destroy_pool(h)
+
+
+def test_noalloc_rejects_partials_past_its_scratch():
+    """The no-allocation call checks its 16 MiB limit on the host before any HIP call."""
+    st, h = _create(num_pages=8192, partition_pages=1)       # 52 splits of 5 pages
+    need = ctypes.c_size_t()
+    assert LIB.paged_attn_workspace_bytes(h, 8, 5, 32, 4101, ctypes.byref(need)) == 0
+    assert need.value > 16 << 20
+    st = LIB.paged_attn_verify_noalloc(h, 0x40000, B.PA_BF16, 0x50000, 0x60000, 257, 0x70000,
+                                       4101, 8, 5, 32, 0.088, None)
+    assert st == B.PA_ERR_WORKSPACE and b"16 MiB" in LIB.paged_attn_last_error()
+    assert LIB.paged_attn_verify_noalloc(None, 0x40000, B.PA_BF16, 0x50000, 0x60000, 257,
+                                         0x70000, 4101, 8, 5, 32, 0.088, None) == B.PA_ERR_INVALID_ARG
+    LIB.paged_attn_destroy_pool(h)

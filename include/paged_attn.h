@@ -262,16 +262,20 @@ pa_status paged_attn_append_kv(const pa_pool* pool, const void* k_new, const voi
  * One token is then drawn with u = u_sample[b] from the weights
  *   w = max(0, p[b][r] - q[b][r]) after a rejection (p[b][r] itself when that
  *       residual is all zero), or w = p[b][num_drafts] when all drafts pass,
- * as the first j at which the running binary64 sum of w exceeds u * sum(w).
- * The running sum is taken in one fixed order (64-entry runs, then their
- * totals, then 4096-entry chunk totals, each left to right), so it rises only
- * on positive weights: a zero-weight token is never drawn.  A row with no
- * mass gives token -1.  p and q rows must be finite and >= 0; a draft token
- * outside [0, vocab) is clamped (the result is then unspecified).
+ * as the first j with w[0] + ... + w[j] > u * (w[0] + ... + w[vocab - 1]),
+ * decided exactly: every float32 is an integer multiple of 2^-149, and the
+ * weights, their running sums and floor(u * total) are formed as integers
+ * (192 bits), with no rounding, so the token does not depend on how the sums
+ * are associated.  The running sum rises only on positive weights: a
+ * zero-weight token is never drawn.  A row with no mass gives token -1.
+ * Entries of p and q must be finite, >= 0 and below 2^22 (probabilities are);
+ * other values, or a draft token outside [0, vocab) (clamped), leave the
+ * result unspecified but never make an access outside the arrays.
  * Limits: num_drafts <= 64, vocab <= 1,048,576, batch <= 65535.  Workspace:
- * paged_attn_rejection_sample_workspace_bytes(batch, vocab) bytes (two
- * binary64 per 4096-entry chunk of a row, then one int32, per sequence), 8-byte
- * aligned, no initial contents.  Two kernels on `stream`; asynchronous. */
+ * paged_attn_rejection_sample_workspace_bytes(batch, vocab) bytes (per
+ * 4096-entry chunk of a row, the exact sums of the weights and of p as twelve
+ * uint32; then one int32 per sequence), 4-byte aligned, no initial contents.
+ * Two kernels on `stream`; asynchronous. */
 size_t paged_attn_rejection_sample_workspace_bytes(int32_t batch, int32_t vocab);
 pa_status paged_attn_rejection_sample(const float* p, const float* q, const int32_t* draft,
                                       const float* u_accept, const float* u_sample,

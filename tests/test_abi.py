@@ -184,10 +184,11 @@ def _sample(p=0x40000, q=0x50000, draft=0x60000, ua=0x70000, us=0x80000, batch=4
 
 
 def test_sample_workspace_bytes():
-    # two binary64 sums per 4096-entry chunk, then one int32 per sequence
-    assert pa.paged_attn_rejection_sample_workspace_bytes(64, 128256) == 64 * 32 * 16 + 64 * 4
-    assert pa.paged_attn_rejection_sample_workspace_bytes(1, 4096) == 16 + 4
-    assert pa.paged_attn_rejection_sample_workspace_bytes(1, 4097) == 32 + 4
+    # two exact sums (six uint32 columns each) per 4096-entry chunk, then one
+    # int32 per sequence
+    assert pa.paged_attn_rejection_sample_workspace_bytes(64, 128256) == 64 * 32 * 48 + 64 * 4
+    assert pa.paged_attn_rejection_sample_workspace_bytes(1, 4096) == 48 + 4
+    assert pa.paged_attn_rejection_sample_workspace_bytes(1, 4097) == 96 + 4
     assert pa.paged_attn_rejection_sample_workspace_bytes(0, 10) == 0
 
 
@@ -203,8 +204,8 @@ def test_sample_workspace_bytes():
     (dict(vocab=(1 << 20) + 1), B.PA_ERR_UNSUPPORTED),
     (dict(batch=65536), B.PA_ERR_UNSUPPORTED),
     (dict(ws=None), B.PA_ERR_WORKSPACE),
-    (dict(ws_bytes=64 * 32 * 16 - 1, batch=64), B.PA_ERR_WORKSPACE),
-    (dict(ws=0xB0004), B.PA_ERR_INVALID_ARG),                    # misaligned workspace
+    (dict(ws_bytes=64 * 32 * 48 - 1, batch=64), B.PA_ERR_WORKSPACE),
+    (dict(ws=0xB0002), B.PA_ERR_INVALID_ARG),                    # misaligned workspace
 ])
 def test_sample_rejects_before_launch(kw, status):
     assert _sample(**kw) == status

@@ -47,6 +47,7 @@ import workloads as W
 METRIC = "decode attention effective HBM GB/s (% of peak) + tokens/s, B=64 ctx=2048"
 PEAK_HBM_GBS = 8000.0
 FLUSH_BYTES = 1 << 30
+HOST_THREADS_PER_GPU = 16
 
 
 def log(msg):
@@ -133,8 +134,10 @@ def cpu_baseline(case, reps):
     import concurrent.futures as cf
     import oracle
 
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    cores = max(1, min(cores, 16))
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    # the host share that goes with one GPU on the MI355X boxes is 16 threads,
+    # whatever os.cpu_count() reports; a larger pool is not allowed there
+    cores = max(1, min(affinity, HOST_THREADS_PER_GPU))
 
     def one(b):
         oracle.paged_attention(case.k_pool, case.v_pool, case.kv_dtype, case.q, case.q_dtype,
@@ -168,20 +171,32 @@ def cpu_baseline(case, reps):
                       f"median {t:.3f} s, float64 C oracle, one sequence per thread",
             "tokens_per_s": case.batch * case.q_per_seq / t,
             "cpu_model": cpu_model(),
+            "host_cpus": {"os_cpu_count": os.cpu_count(), "affinity": affinity,
+                          "threads_allowed": HOST_THREADS_PER_GPU},
             "single_thread": {"value": case.algorithmic_bytes(seqs=range(k)) / t1 / 1e9,
                               "unit": "GB/s", "cores": 1,
                               "sample": f"sequences 0..{k - 1} of {case.batch}, once, {t1:.2f} s"}}
 
 
 def cpu_model():
-    """The host CPU's model name (Linux), or None."""
+    """The host CPU as /proc/cpuinfo names it: model name, family, model and
+    stepping (a virtual machine may report only the vendor's family name), or
+    None."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            key, _, val = line.partition(":")
+            key = key.strip()
+            if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                fields[key] = val.strip()
+            if not line.strip() and fields:
+                break
     except OSError:
-        pass
-    return None
+        return None
+    if not fields:
+        return None
+    ident = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{fields.get('model name', '?')} ({ident})" if ident else fields.get("model name")
 
 
 def append_bytes(case, n_new, src_dtype, seq_lens=None):
@@ -394,6 +409,23 @@ def measure_copy_gbs(torch, stream):
     return gbs
 
 
+def measure_read_gbs(torch, stream, flush_caches):
+    """The box's read-stream bandwidth in the same run: the bench's own 1 GiB
+    cache-flush read (torch's sum over it), timed with HIP events on `stream`,
+    best of ten.  A read-only denominator next to the copy rate (a copy mixes
+    reads and writes and runs slower)."""
+    best = None
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flush_caches()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return FLUSH_BYTES / (best / 1e3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -539,6 +571,12 @@ def main():
     if not mfma_bound:
         result["pct_of_copy"] = round(100 * gbs / copy_gbs, 2)
         result["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
+    if flush is not None:
+        read_gbs = measure_read_gbs(torch, stream, flush_caches)
+        result["read_gbs"] = round(read_gbs, 1)
+        if not mfma_bound:
+            result["pct_of_read"] = round(100 * gbs / read_gbs, 2)
+            result["roofline"]["frac_of_read"] = round(achieved / read_gbs, 4)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(case, args.cpu_reps)

@@ -40,8 +40,10 @@
  * (kv fp8-e4m3, q bf16).  page_size must be 16 and head_dim 128.
  *
  * Ownership: every buffer belongs to the caller.  The library allocates no
- * device memory; a pool handle only records the descriptor (a few dozen
- * bytes of host memory) and never frees the caller's arrays.
+ * device memory (paged_attn_verify_noalloc uses a static array of the
+ * library's code object instead of a workspace); a pool handle only records
+ * the descriptor (a few dozen bytes of host memory) and never frees the
+ * caller's arrays.
  *
  * Calls: asynchronous on the given stream (a hipStream_t; NULL = the null
  * stream of the current device) on the current HIP device.  Argument checks
@@ -133,6 +135,10 @@ pa_status paged_attn_pool_bytes(int32_t num_pages, int32_t page_size,
                                 pa_dtype kv_dtype, size_t* k_bytes, size_t* v_bytes);
 
 /* Checks the descriptor and returns a handle recording it (host only, no HIP call).
+ * The pool is the shared set of equal-size 16-token blocks that every
+ * sequence's block table points into ("Batching, speculative decoding, paged
+ * attention" §5.3.7; "Latency and cost in production" §10.12.2: blocks are
+ * taken from one pool on demand and returned when a request ends).
  * PA_ERR_INVALID_ARG for null pointers or counts < 1, PA_ERR_UNSUPPORTED for
  * page_size != 16, head_dim != 128 or an unknown dtype; *out is NULL on error. */
 pa_status paged_attn_create_pool(const pa_pool_desc* desc, pa_pool** out);
@@ -153,9 +159,14 @@ pa_status paged_attn_workspace_bytes(const pa_pool* pool, int32_t batch,
                                      int32_t q_per_seq, int32_t num_q_heads,
                                      int32_t max_seq_len, size_t* bytes);
 
-/* Decode: one query row per sequence (q_per_seq = 1).  The newest token's K/V
- * must already be in the pool (seq_lens counts it).  max_seq_len is a host-side
- * upper bound of seq_lens used to size the split. */
+/* Decode: one query row per sequence (q_per_seq = 1), attending to every key
+ * of its sequence through the block table ("Latency and cost in production"
+ * §10.3.1: the new token's query is compared with every earlier key; "Batching,
+ * speculative decoding, paged attention" §5.3.1 and §5.3.7: a decode step reads
+ * each request's whole KV cache, gathered block by block).  The newest token's
+ * K/V must already be in the pool (seq_lens counts it).  max_seq_len is a
+ * host-side upper bound of seq_lens used to size the split.  Errors as
+ * paged_attn_verify. */
 pa_status paged_attn_decode(const pa_pool* pool, const void* q, pa_dtype q_dtype,
                             void* out, const int32_t* block_table,
                             int32_t max_pages_per_seq, const int32_t* seq_lens,
@@ -165,7 +176,17 @@ pa_status paged_attn_decode(const pa_pool* pool, const void* q, pa_dtype q_dtype
 
 /* Verify: q_per_seq = K + 1 query rows per sequence (the last accepted token
  * and the K drafts, whose K/V are already appended), scored in one call under
- * the causal mask described at the top of this file. */
+ * the causal mask described at the top of this file ("Speculative decoding
+ * principles" 7.2.1, "the four steps of one iteration": the target scores the
+ * context and the K drafts in one forward, each position seeing only itself
+ * and earlier positions).  Returns PA_ERR_INVALID_ARG for null pointers, counts
+ * < 1, num_q_heads not a multiple of the pool's KV heads, max_seq_len <
+ * q_per_seq or > 16 * max_pages_per_seq, a non-finite scale or misaligned q / k
+ * / v (16 bytes) or out (element size); PA_ERR_UNSUPPORTED for a (kv, q) dtype
+ * pair outside the three supported; PA_ERR_WORKSPACE when the plan splits and
+ * the workspace is missing, smaller than paged_attn_workspace_bytes() or not
+ * 256-byte aligned; PA_ERR_HIP if a launch fails.  Nothing is launched on an
+ * error. */
 pa_status paged_attn_verify(const pa_pool* pool, const void* q, pa_dtype q_dtype,
                             void* out, const int32_t* block_table,
                             int32_t max_pages_per_seq, const int32_t* seq_lens,

@@ -16,7 +16,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCE = os.path.join(_HERE, "oracle.c")
+# ORACLE_LIB names another build of oracle.c to load (the sanitizer test's)
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, E4M3 = 0, 1, 2
 _CODES = {"f32": F32, "bf16": BF16, "fp8": E4M3}
@@ -24,16 +26,26 @@ _CODES = {"f32": F32, "bf16": BF16, "fp8": E4M3}
 _lib = None
 
 
+GCC_FLAGS = ["-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-fno-fast-math"]
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (strict IEEE, no fast-math)."""
     if force or not os.path.exists(LIB_PATH):
-        src = os.path.join(_HERE, "oracle.c")
         tmp = LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
-               "-fno-fast-math", src, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
+        subprocess.run(["gcc", "-O2", *GCC_FLAGS, SOURCE, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def build_sanitized(path: str) -> str:
+    """oracle.c built with AddressSanitizer and UndefinedBehaviorSanitizer (host
+    code, gcc), every finding fatal; load it by running the tests with
+    ORACLE_LIB=path and gcc's libasan preloaded."""
+    subprocess.run(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", *GCC_FLAGS, SOURCE, "-o", path, "-lm"],
+                   check=True)
+    return path
 
 
 def _load():

@@ -411,9 +411,10 @@ def measure_copy_gbs(torch, stream):
 
 def measure_read_gbs(torch, stream, flush_caches):
     """The box's read-stream bandwidth in the same run: the bench's own 1 GiB
-    cache-flush read (torch's sum over it), timed with HIP events on `stream`,
-    best of ten.  A read-only denominator next to the copy rate (a copy mixes
-    reads and writes and runs slower)."""
+    cache-flush read (torch's float64 sum over it), timed with HIP events on
+    `stream`, best of ten.  A read-only denominator next to the copy rate (a
+    copy mixes reads and writes and runs slower); a reduction kernel of
+    torch's, so a lower bound of what a plain read stream reaches."""
     best = None
     for _ in range(10):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -424,6 +425,25 @@ def measure_read_gbs(torch, stream, flush_caches):
         ms = e0.elapsed_time(e1)
         best = ms if best is None else min(best, ms)
     return FLUSH_BYTES / (best / 1e3) / 1e9
+
+
+def measure_read_us(torch, stream, flush_caches, nbytes):
+    """Time of one plain read of `nbytes` from HBM (torch's float64 sum over a
+    buffer of that size, the caches flushed first), median of ten, with HIP
+    events on `stream`."""
+    buf = torch.ones(max(nbytes // 8, 1), dtype=torch.float64, device="cuda")
+    times = []
+    for _ in range(10):
+        flush_caches()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        buf.sum()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del buf
+    torch.cuda.empty_cache()
+    return float(np.median(times))
 
 
 def main():
@@ -450,8 +470,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     def flush_caches():
+        # a read of the whole 1 GiB buffer (as float64: a quarter of the elements
+        # of its bf16 view, so the reduction keeps up with HBM)
         if flush is not None:
-            flush.sum(dtype=torch.float32)
+            flush.view(torch.float64).sum()
 
     if args.op == "sample":
         bench_sample(args, torch, pa, flush_caches, stream)
@@ -577,6 +599,10 @@ def main():
         if not mfma_bound:
             result["pct_of_read"] = round(100 * gbs / read_gbs, 2)
             result["roofline"]["frac_of_read"] = round(achieved / read_gbs, 4)
+            # the same number of bytes read as one plain stream, from HBM, with its
+            # own launch and ramp: what a call of this size costs at the least
+            same_us = measure_read_us(torch, stream, flush_caches, nbytes)
+            result["read_same_bytes_us"] = round(same_us, 2)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(case, args.cpu_reps)

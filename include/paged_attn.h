@@ -74,13 +74,19 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels handle */
     PA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
     PA_ERR_HIP = -4,          /* a HIP runtime call failed; see paged_attn_last_error() */
-    PA_ERR_CONTRACT = -5      /* paged_attn_validate found a bad device array */
+    PA_ERR_CONTRACT = -5,     /* paged_attn_validate found a bad device array */
+    /* not a status: makes every int32 value a value of the type, so an arbitrary
+       code a caller passes (paged_attn_status_str) is well defined */
+    PA_STATUS_INT32_RANGE = 0x7fffffff
 } pa_status;
 
 typedef enum pa_dtype {
     PA_F32 = 0,
     PA_BF16 = 1,
-    PA_FP8_E4M3 = 2
+    PA_FP8_E4M3 = 2,
+    /* not a dtype: makes every int32 value a value of the type, so an unknown
+       code is rejected (PA_ERR_UNSUPPORTED / PA_ERR_INVALID_ARG), not undefined */
+    PA_DTYPE_INT32_RANGE = 0x7fffffff
 } pa_dtype;
 
 /* Description of a page pool.  All pointers are device pointers. */

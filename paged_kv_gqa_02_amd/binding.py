@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpaged_attn.so")
+# PAGED_ATTN_LIB names another build of the same sources to load (the host
+# sanitizer test's); by default the in-tree library
+LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or os.path.join(PKG, "libpaged_attn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "paged_attn.h")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CONTRACT = \

@@ -35,27 +35,45 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False) -> str:
+# Host code only (the argument checks, the launch plan, the C ABI): AddressSanitizer
+# and UndefinedBehaviorSanitizer, every finding fatal.  The device code is built
+# as usual.  The sanitizer runtime is not linked in; the process that loads such
+# a build preloads clang's (see HOST_SANITIZER_RUNTIME).
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all",
+                       "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def host_sanitizer_runtime():
+    """clang's shared AddressSanitizer runtime of this ROCm, or None."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build(verbose: bool = False, out: str = LIB, host_sanitize: bool = False) -> str:
     """Compile every source to an object (each with its own flags), then link."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmpdir = tempfile.mkdtemp(prefix="paged_attn_build_")
+    san = HOST_SANITIZE_FLAGS if host_sanitize else []
     try:
         objs, notes = [], []
         for src in SRCS:
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
             extra = FILE_FLAGS.get(os.path.basename(src), [])
-            notes.append(_run([hipcc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-c", src, "-o", obj]))
+            notes.append(_run([hipcc, *HIPCC_FLAGS, *extra, *san, "-I", INCLUDE, "-c", src, "-o",
+                               obj]))
             objs.append(obj)
-        tmp = LIB + ".tmp"
+        tmp = out + ".tmp"
         notes.append(_run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     if verbose:
         for n in notes:
             if n.strip():
                 print(n, file=sys.stderr)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

@@ -57,7 +57,7 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode8b", choices=W.WORKLOADS)
     ap.add_argument("--kv-dtype", default=None, choices=("bf16", "fp8", "f32"),
@@ -127,6 +127,14 @@ def measured_traffic(key):
     if rec.get("code_sha256") != digest:
         return None
     return int(round(rec["traffic_bytes"]))
+
+
+def add_speedup(result):
+    """The GPU rate over the oracle's (same unit, same byte or FLOP formula) as
+    cpu_baseline.gpu_speedup: a stated ratio, not a measure of kernel quality."""
+    cpu = result.get("cpu_baseline")
+    if cpu and cpu.get("unit") == result["unit"] and cpu["value"] > 0:
+        cpu["gpu_speedup"] = round(result["value"] / cpu["value"], 1)
 
 
 def cpu_baseline(case, reps):
@@ -289,6 +297,7 @@ def bench_append(args, torch, pa, case, dev, pool, flush_caches, stream):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_append_baseline(case, kn, vn, src, n_new)
+    add_speedup(result)
     print(json.dumps(result), flush=True)
 
 
@@ -372,6 +381,7 @@ def bench_sample(args, torch, pa, flush_caches, stream):
             "value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"whole batch, {len(times)} reps, median {t * 1e3:.2f} ms, one thread",
             "tokens_per_s": float((accepted + 1).sum()) / t}
+    add_speedup(result)
     print(json.dumps(result), flush=True)
 
 
@@ -610,6 +620,7 @@ def main():
             sec = case.algorithmic_bytes() / (cpu["value"] * 1e9)
             cpu.update({"value": flops / sec / 1e12, "unit": "TFLOP/s"})
         result["cpu_baseline"] = cpu
+    add_speedup(result)
     print(json.dumps(result), flush=True)
 
 

@@ -49,7 +49,11 @@
  * stream of the current device) on the current HIP device.  Argument checks
  * run on the host before anything is launched and return an error without
  * launching.  Calls are reentrant; a pool handle is read-only after
- * creation and may be shared across threads.
+ * creation and may be shared across threads.  Apart from paged_attn_validate,
+ * which copies to the host and synchronises, a call only enqueues kernels on
+ * `stream` (no memset, copy, allocation or synchronisation), so it may be
+ * captured into a HIP graph and replayed; the graph then reads whatever the
+ * captured buffers hold at each replay.
  *
  * Device-array contract (not checked on the fast path; paged_attn_validate
  * checks it): for every b, n <= seq_lens[b] <= max_seq_len <=
@@ -72,7 +76,7 @@ typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = -1,  /* null pointer, bad size or count */
     PA_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels handle */
-    PA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+    PA_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned */
     PA_ERR_HIP = -4,          /* a HIP runtime call failed; see paged_attn_last_error() */
     PA_ERR_CONTRACT = -5,     /* paged_attn_validate found a bad device array */
     /* not a status: makes every int32 value a value of the type, so an arbitrary

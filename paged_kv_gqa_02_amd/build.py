@@ -35,27 +35,34 @@ def _run(cmd):
     return err
 
 
-# Host code only (the argument checks, the launch plan, the C ABI): AddressSanitizer
-# and UndefinedBehaviorSanitizer, every finding fatal.  The device code is built
-# as usual.  The sanitizer runtime is not linked in; the process that loads such
-# a build preloads clang's (see HOST_SANITIZER_RUNTIME).
-HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
-                       "-Xarch_host", "-fno-sanitize-recover=all",
-                       "-Xarch_host", "-fno-omit-frame-pointer"]
+# Host code only (the argument checks, the launch plan, the C ABI): sanitizer
+# builds for the CPU tests, every finding fatal.  The device code is built as
+# usual.  The sanitizer runtime is not linked in; the process that loads such a
+# build preloads clang's (host_sanitizer_runtime).  "address":
+# AddressSanitizer and UndefinedBehaviorSanitizer; "thread": ThreadSanitizer.
+HOST_SANITIZE_FLAGS = {
+    "address": ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-sanitize-recover=all",
+                "-Xarch_host", "-fno-omit-frame-pointer"],
+    "thread": ["-Xarch_host", "-fsanitize=thread", "-Xarch_host", "-fno-omit-frame-pointer"],
+}
+_RUNTIME = {"address": "asan", "thread": "tsan"}
 
 
-def host_sanitizer_runtime():
-    """clang's shared AddressSanitizer runtime of this ROCm, or None."""
+def host_sanitizer_runtime(kind: str = "address"):
+    """clang's shared runtime of this ROCm for the sanitizer `kind`, or None."""
     import glob
-    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    name = f"libclang_rt.{_RUNTIME[kind]}-x86_64.so"
+    hits = sorted(glob.glob(f"/opt/rocm/llvm/lib/clang/*/lib/linux/{name}"))
     return hits[-1] if hits else None
 
 
-def build(verbose: bool = False, out: str = LIB, host_sanitize: bool = False) -> str:
-    """Compile every source to an object (each with its own flags), then link."""
+def build(verbose: bool = False, out: str = LIB, host_sanitize: str | None = None) -> str:
+    """Compile every source to an object (each with its own flags), then link.
+    host_sanitize: None, "address" or "thread" (a host-code sanitizer build)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmpdir = tempfile.mkdtemp(prefix="paged_attn_build_")
-    san = HOST_SANITIZE_FLAGS if host_sanitize else []
+    san = HOST_SANITIZE_FLAGS[host_sanitize] if host_sanitize else []
     try:
         objs, notes = [], []
         for src in SRCS:

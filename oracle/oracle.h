@@ -22,7 +22,7 @@
  *  - "Latency and cost in production" §10.8.2-§10.8.3: real ~= (q - zp) *
  *    scale, symmetric quantisation has zp = 0.
  *
- * Readings where the pages are silent (restated in the design doc):
+ * Readings where the pages are silent:
  *  - softmax uses the natural exponential of scale * q.k;
  *  - seq_lens[b] counts every key already in the pool, including the n new
  *    query tokens; row i (0 <= i < n) sees keys 0 .. L - n + i inclusive;

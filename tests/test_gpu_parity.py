@@ -544,3 +544,19 @@ def test_gqa_mapping_with_constant_values(pa, kv, n):
     err = float(np.abs(out - want[None, None, :, None]).max())
     say(f"    GQA mapping {kv} n={n}: max_abs={err:.3e}")
     assert err <= (1e-5 if kv == "f32" else 1e-6)
+
+
+@pytest.mark.parametrize("name,batch,n,hq,hkv,kv,lo,hi", [
+    ("decode", 2048, 1, 32, 8, "bf16", 1, 300),
+    ("verify", 1024, 5, 32, 8, "bf16", 5, 700),
+])
+def test_large_batches(pa, name, batch, n, hq, hkv, kv, lo, hi):
+    """Serving-sized batches of short ragged sequences (grids of 8,192 to 16,384
+    workgroups), every sequence against the oracle."""
+    rng = np.random.default_rng(300 + batch)
+    lens = [int(x) for x in rng.integers(lo, hi + 1, size=batch)]
+    case = W.make_case(f"large-{name}", batch=batch, q_per_seq=n, num_q_heads=hq,
+                       num_kv_heads=hkv, seq_lens=lens, kv_dtype=kv, q_dtype="bf16",
+                       seed=400 + batch)
+    gpu = run_gpu(pa, case, label="large batch")
+    check(gpu, oracle_all(case), kv, f"{name}, batch {batch}, all sequences")

@@ -95,3 +95,16 @@ def test_sampler_rejects_output_shapes():
     with pytest.raises(ValueError, match="num_accepted"):
         pa.paged_attn_rejection_sample(p, q, d, ua, us,
                                        num_accepted=torch.zeros(2, dtype=torch.int64))
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """No fallback: with the HIP library absent, importing the package raises."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PAGED_ATTN_LIB=str(tmp_path / "absent" / "libpaged_attn.so"))
+    res = subprocess.run([sys.executable, "-c", "import paged_kv_gqa_02_amd"], cwd=root, env=env,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode != 0
+    assert "ImportError" in res.stderr and "is missing" in res.stderr, res.stderr[-2000:]

@@ -55,6 +55,10 @@
  * captured into a HIP graph and replayed; the graph then reads whatever the
  * captured buffers hold at each replay.
  *
+ * Batch order: sequences are taken in index order.  On a mix of lengths a
+ * batch ordered longest first finishes sooner (no long sequence is left for
+ * the end of the grid); results do not depend on the order.
+ *
  * Device-array contract (not checked on the fast path; paged_attn_validate
  * checks it): for every b, n <= seq_lens[b] <= max_seq_len <=
  * 16 * max_pages_per_seq, and block_table[b][p] lies in [0, num_pages) for
